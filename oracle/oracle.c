@@ -1,0 +1,453 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU implementation of the binary sign-GEMV
+ * path, written in double precision.  Only tests/, __graft_entry__.smoke()
+ * and bench.py's cpu_baseline leg may load it.  It shares no code, header,
+ * table or helper with the HIP library under bit_gemv_packed_amd/csrc; the
+ * physical-layout formula below is a second, independent implementation of
+ * the formula documented in include/bsg.h.
+ *
+ * Sources (the web pages this path is built from):
+ *  [BiLoCo]  "BiLoCo: Binary Low-Rank Corrections for Post-Training
+ *            Quantization", sections "The core idea" (alpha*u*(v.x) computed
+ *            with additions only; worked example) and "Finding the sign
+ *            vectors" (error-minimising coefficient).
+ *  [FluxBin] "FluxBin: Flexible LUT-based Ultra-low-bit LLM Inference by
+ *            Algorithm-Kernel Synergy", Sec. 2 (greedy residual binary bases,
+ *            R(k) = R(k-1) - alpha_k B(k)), Sec. 3.1 (decoupled row/column
+ *            scales; quantised matrix is the sum of the bases), Sec. 3.2
+ *            Stage 1 (bits map to signs by 2b-1).
+ *  [BiSCo]   "BiSCo-LLM: Lookup-Free Binary Spherical Coding ...", technical
+ *            summary, "Sensitivity Protection" (about 1% of sensitive channels
+ *            chosen from activation statistics and weight magnitudes, stored
+ *            in 8 bits apart from the binary payload).
+ *
+ * Conventions (readings where the pages are silent; each is listed in
+ * the design doc):
+ *  - logical bits: word w of row m of base k holds columns 32w..32w+31, bit j
+ *    of the word is column 32w+j (LSB first); a set bit is +1, a clear bit -1.
+ *  - every sum runs in double, in ascending index order, one bit at a time.
+ *  - fp16 / fp32 roundings are round-to-nearest-even.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math, no FMA
+ * contraction, so every rounding below is the one written).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+#define OR_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------ */
+/* IEEE-754 binary16 conversions, written from the format definition.  */
+/* ------------------------------------------------------------------ */
+
+/* binary16 bit pattern -> exact double value. */
+OR_API double or_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int exp = (h >> 10) & 0x1f;
+  int frac = h & 0x3ff;
+  double v;
+  if (exp == 0) {
+    v = ldexp((double)frac, -24);                 /* subnormal: frac * 2^-24 */
+  } else if (exp == 31) {
+    v = frac ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(frac | 0x400), exp - 25);  /* 1.frac * 2^(exp-15) */
+  }
+  return sign ? -v : v;
+}
+
+/* binary32 value -> binary16 bit pattern, round to nearest, ties to even. */
+OR_API uint16_t or_f32_to_f16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  uint32_t exp = (u >> 23) & 0xffu;
+  uint32_t man = u & 0x7fffffu;
+  if (exp == 0xff) return (uint16_t)(sign | 0x7c00u | (man ? 0x200u : 0u));
+  /* value = 1.man * 2^(exp-127) (normal) or 0.man * 2^-126 (subnormal) */
+  if (exp == 0) return sign;  /* fp32 subnormals are far below fp16's least subnormal */
+  int e = (int)exp - 127;     /* unbiased exponent */
+  uint32_t sig = man | 0x800000u; /* 24-bit significand, value = sig * 2^(e-23) */
+  if (e > 15) return (uint16_t)(sign | 0x7c00u);   /* overflow -> inf */
+  int shift;                   /* bits of sig to drop */
+  uint32_t base_exp;
+  if (e >= -14) {              /* fp16 normal range: keep 11 significant bits */
+    shift = 13;
+    base_exp = (uint32_t)(e + 15);
+  } else {                     /* fp16 subnormal: value = q * 2^-24 */
+    shift = 13 + (-14 - e);
+    base_exp = 0;
+    if (shift > 24) return sign; /* rounds to zero (below half the least subnormal) */
+  }
+  uint32_t q = sig >> shift;
+  uint32_t rem = sig & ((1u << shift) - 1u);
+  uint32_t half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (q & 1u))) q += 1u;
+  uint32_t out;
+  if (base_exp == 0) {
+    out = q;                   /* q <= 0x400; 0x400 is the least normal, encoded correctly */
+  } else {
+    /* q in [0x400, 0x800]; carry into the exponent when it reaches 0x800 */
+    if (q >= 0x800u) { q >>= 1; base_exp += 1; }
+    if (base_exp >= 31) return (uint16_t)(sign | 0x7c00u);
+    out = (base_exp << 10) | (q & 0x3ffu);
+  }
+  return (uint16_t)(sign | out);
+}
+
+/* ------------------------------------------------------------------ */
+/* The product itself.                                                 */
+/* ------------------------------------------------------------------ */
+
+static inline int or_bit(const uint32_t* row_words, int n) {
+  return (int)((row_words[n >> 5] >> (n & 31)) & 1u);
+}
+
+/*
+ * Binary-base product [FluxBin Sec. 3.1, Sec. 3.2 Stage 1]:
+ *   y[m,b] = sum_k alpha[k][m] * sum_n (2 bit_k(m,n) - 1) * c_k[n] * x[n,b]
+ * bits: logical [K][M][ceil(N/32)]; alpha [K][M]; colscale [K][N] or NULL
+ * (then c == 1); x [N][B]; y [M][B] (overwritten).  Any N >= 0.
+ */
+OR_API void or_sign_gemv(const uint32_t* bits, int K, int M, int N,
+                         const double* alpha, const double* colscale,
+                         const double* x, int B, double* y) {
+  int nd = (N + 31) / 32;
+  for (int m = 0; m < M; ++m) {
+    for (int b = 0; b < B; ++b) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) {
+        const uint32_t* row = bits + ((size_t)k * M + m) * nd;
+        double s = 0.0;
+        for (int n = 0; n < N; ++n) {
+          double sgn = or_bit(row, n) ? 1.0 : -1.0;
+          double c = colscale ? colscale[(size_t)k * N + n] : 1.0;
+          s += sgn * c * x[(size_t)n * B + b];
+        }
+        acc += alpha[(size_t)k * M + m] * s;
+      }
+      y[(size_t)m * B + b] = acc;
+    }
+  }
+}
+
+/*
+ * Binary low-rank correction [BiLoCo, "The core idea"]:
+ *   z[j,b]  = alpha_r[j] * sum_n sv(j,n) * x[n,b]
+ *   y[m,b]  = sum_j su(m,j) * z[j,b]
+ * U: logical [M][ceil(r/32)] (row m holds u_j[m] for j = 0..r-1),
+ * V: logical [r][ceil(N/32)], alpha_r [r]; y [M][B] overwritten.
+ */
+OR_API void or_binlr(const uint32_t* ubits, const uint32_t* vbits,
+                     const double* alpha_r, int r, int M, int N,
+                     const double* x, int B, double* y) {
+  int nd = (N + 31) / 32, rd = (r + 31) / 32;
+  double* z = (double*)calloc((size_t)(r > 0 ? r : 1) * (B > 0 ? B : 1), sizeof(double));
+  for (int j = 0; j < r; ++j)
+    for (int b = 0; b < B; ++b) {
+      double s = 0.0;
+      for (int n = 0; n < N; ++n)
+        s += (or_bit(vbits + (size_t)j * nd, n) ? 1.0 : -1.0) * x[(size_t)n * B + b];
+      z[(size_t)j * B + b] = alpha_r[j] * s;
+    }
+  for (int m = 0; m < M; ++m)
+    for (int b = 0; b < B; ++b) {
+      double s = 0.0;
+      for (int j = 0; j < r; ++j)
+        s += (or_bit(ubits + (size_t)m * rd, j) ? 1.0 : -1.0) * z[(size_t)j * B + b];
+      y[(size_t)m * B + b] = s;
+    }
+  free(z);
+}
+
+/*
+ * Protected int8 rows [BiSCo, "Sensitivity Protection"]:
+ *   y[rows[i], b] = s[i] * sum_n q[i][n] * x[n,b]; every other row is 0.
+ * y [M][B] overwritten.  Rows outside [0, M) are skipped.
+ */
+OR_API void or_salient(const int32_t* rows, int ns, const int8_t* q, const double* s,
+                       int M, int N, const double* x, int B, double* y) {
+  memset(y, 0, sizeof(double) * (size_t)M * (B > 0 ? B : 0));
+  for (int i = 0; i < ns; ++i) {
+    int m = rows[i];
+    if (m < 0 || m >= M) continue;
+    for (int b = 0; b < B; ++b) {
+      double acc = 0.0;
+      for (int n = 0; n < N; ++n) acc += (double)q[(size_t)i * N + n] * x[(size_t)n * B + b];
+      y[(size_t)m * B + b] += s[i] * acc;
+    }
+  }
+}
+
+/*
+ * Integer sign product for int8 activations (exact):
+ *   acc[k][m][b] = sum_n (2 bit_k(m,n) - 1) * xq[n,b]   (int64)
+ */
+OR_API void or_sign_gemv_i8(const uint32_t* bits, int K, int M, int N,
+                            const int8_t* xq, int B, int64_t* acc) {
+  int nd = (N + 31) / 32;
+  for (int k = 0; k < K; ++k)
+    for (int m = 0; m < M; ++m) {
+      const uint32_t* row = bits + ((size_t)k * M + m) * nd;
+      for (int b = 0; b < B; ++b) {
+        int64_t s = 0;
+        for (int n = 0; n < N; ++n)
+          s += (or_bit(row, n) ? 1 : -1) * (int64_t)xq[(size_t)n * B + b];
+        acc[((size_t)k * M + m) * B + b] = s;
+      }
+    }
+}
+
+/*
+ * Symmetric per-column int8 quantisation of activations (the caller's rule
+ * for the int8 mode; a reading, the pages fix none):
+ *   sx[b] = fp32( max_n |x[n,b]| / 127 )     (fp32 division)
+ *   xq    = clamp( rint_half_even( fp32(x / sx) ), -127, 127 ), 0 if sx == 0
+ * x holds fp32 values [N][B].
+ */
+OR_API void or_quantize_i8(const float* x, int N, int B, int8_t* xq, float* sx) {
+  for (int b = 0; b < B; ++b) {
+    float mx = 0.0f;
+    for (int n = 0; n < N; ++n) {
+      float a = fabsf(x[(size_t)n * B + b]);
+      if (a > mx) mx = a;
+    }
+    volatile float s = mx / 127.0f;
+    sx[b] = s;
+    for (int n = 0; n < N; ++n) {
+      int8_t v = 0;
+      if (s != 0.0f) {
+        volatile float t = x[(size_t)n * B + b] / s;
+        float r = nearbyintf(t);  /* default rounding mode: nearest, ties to even */
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        v = (int8_t)r;
+      }
+      xq[(size_t)n * B + b] = v;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Packing (offline): greedy residual binary bases.                     */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Greedy residual bases [FluxBin Sec. 2, QBB/DB-LLM residual; Sec. 3.1 row
+ * and column scales], in the pages' order, one base at a time:
+ *   R <- W
+ *   for k = 1..K:
+ *     B_k = sign(R) with sign(0) = +1                     (bit = [R >= 0])
+ *     alpha_k[m] = fp32( (sum_n |R[m,n]|) / N )            (error-minimising
+ *                  row scale for a sign matrix: mean absolute value)
+ *     if colscale: c_k[n] = fp16(fp32( num_n / den )),
+ *                  num_n = sum_m alpha_k[m] |R[m,n]|, den = sum_m alpha_k[m]^2
+ *                  (least-squares column scale given alpha_k and B_k;
+ *                   c = 1 when den == 0), else c_k = 1
+ *     R <- R - alpha_k[m] * c_k[n] * B_k[m,n]   (with the stored, rounded
+ *                                               alpha and c)
+ * Outputs: logical bits [K][M][ceil(N/32)] (padding bits zero), alpha fp32
+ * [K][M], colscale fp16 bits [K][N] (only written when with_colscale).
+ * Returns 0, or -1 on allocation failure, -2 on a NaN in W.
+ */
+OR_API int or_pack(const float* W, int M, int N, int K, int with_colscale,
+                   uint32_t* bits, float* alpha, uint16_t* colscale) {
+  int nd = (N + 31) / 32;
+  size_t mn = (size_t)M * N;
+  double* R = (double*)malloc(sizeof(double) * (mn ? mn : 1));
+  if (!R) return -1;
+  for (size_t i = 0; i < mn; ++i) {
+    if (isnan(W[i])) { free(R); return -2; }
+    R[i] = (double)W[i];
+  }
+  memset(bits, 0, sizeof(uint32_t) * (size_t)K * M * nd);
+  double* cdbl = (double*)malloc(sizeof(double) * (N > 0 ? N : 1));
+  for (int k = 0; k < K; ++k) {
+    uint32_t* bk = bits + (size_t)k * M * nd;
+    float* ak = alpha + (size_t)k * M;
+    /* 1. signs */
+    for (int m = 0; m < M; ++m)
+      for (int n = 0; n < N; ++n)
+        if (R[(size_t)m * N + n] >= 0.0) bk[(size_t)m * nd + (n >> 5)] |= 1u << (n & 31);
+    /* 2. row scales */
+    for (int m = 0; m < M; ++m) {
+      double s = 0.0;
+      for (int n = 0; n < N; ++n) s += fabs(R[(size_t)m * N + n]);
+      ak[m] = (float)(N > 0 ? s / (double)N : 0.0);
+    }
+    /* 3. column scales */
+    for (int n = 0; n < N; ++n) cdbl[n] = 1.0;
+    if (with_colscale) {
+      double den = 0.0;
+      for (int m = 0; m < M; ++m) den += (double)ak[m] * (double)ak[m];
+      for (int n = 0; n < N; ++n) {
+        uint16_t h;
+        if (den == 0.0) {
+          h = 0x3c00u; /* 1.0 */
+        } else {
+          double num = 0.0;
+          for (int m = 0; m < M; ++m) num += (double)ak[m] * fabs(R[(size_t)m * N + n]);
+          h = or_f32_to_f16((float)(num / den));
+        }
+        colscale[(size_t)k * N + n] = h;
+        cdbl[n] = or_f16_to_f64(h);
+      }
+    }
+    /* 4. residual */
+    for (int m = 0; m < M; ++m)
+      for (int n = 0; n < N; ++n) {
+        double sgn = (bk[(size_t)m * nd + (n >> 5)] >> (n & 31)) & 1u ? 1.0 : -1.0;
+        double t = (double)ak[m] * cdbl[n];   /* exact: 24-bit x 11-bit significands */
+        R[(size_t)m * N + n] = R[(size_t)m * N + n] - t * sgn;
+      }
+  }
+  free(cdbl);
+  free(R);
+  return 0;
+}
+
+/*
+ * Pack an arbitrary real matrix into logical sign bits: bit = [S >= 0].
+ * Used for the +-1 low-rank factors U [M][r] and V [r][N].
+ */
+OR_API void or_pack_signs(const float* S, int M, int N, uint32_t* bits) {
+  int nd = (N + 31) / 32;
+  memset(bits, 0, sizeof(uint32_t) * (size_t)M * nd);
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n)
+      if (S[(size_t)m * N + n] >= 0.0f) bits[(size_t)m * nd + (n >> 5)] |= 1u << (n & 31);
+}
+
+/*
+ * Activation statistic for choosing protected rows [BiSCo, "Sensitivity
+ * Protection": activation statistics]:  xbar[n] = fp32( sum_s |X[s][n]| / S ).
+ * X holds S calibration vectors of N fp32 values.
+ */
+OR_API void or_absmean(const float* X, int S, int N, float* xbar) {
+  for (int n = 0; n < N; ++n) {
+    double s = 0.0;
+    for (int i = 0; i < S; ++i) s += fabs((double)X[(size_t)i * N + n]);
+    xbar[n] = (float)(S > 0 ? s / (double)S : 0.0);
+  }
+}
+
+/*
+ * Protected rows [BiSCo, "Sensitivity Protection"]: score each output row by
+ * weight magnitude times activation statistic, keep the ns highest as int8.
+ *   score_m = sum_n |W[m,n]| * xbar[n]              (double, n ascending)
+ *   rows    = the ns largest scores, ties to the smaller m, stored ascending
+ *   s_i     = fp16(fp32( max_n |W[m,n]| / 127 ))     (symmetric, per row)
+ *   q[i,n]  = clamp(rint_half_even(W[m,n] / s_i), -127, 127), 0 if s_i == 0
+ *   alpha[k][m] = 0 for every base k on the kept rows (the int8 row replaces
+ *   the binary row).
+ * Selection is by plain repeated maximum search (O(ns*M)).
+ * Returns 0, -1 if ns is out of range.
+ */
+OR_API int or_salient_select(const float* W, int M, int N, const float* xbar, int ns,
+                             int32_t* rows, int8_t* q, uint16_t* s_f16,
+                             float* alpha, int K) {
+  if (ns < 0 || ns > M) return -1;
+  double* score = (double*)malloc(sizeof(double) * (M > 0 ? M : 1));
+  char* taken = (char*)calloc(M > 0 ? M : 1, 1);
+  for (int m = 0; m < M; ++m) {
+    double s = 0.0;
+    for (int n = 0; n < N; ++n) s += fabs((double)W[(size_t)m * N + n]) * (double)xbar[n];
+    score[m] = s;
+  }
+  for (int i = 0; i < ns; ++i) {
+    int best = -1;
+    for (int m = 0; m < M; ++m) {
+      if (taken[m]) continue;
+      if (best < 0 || score[m] > score[best]) best = m;  /* strict: ties keep the smaller m */
+    }
+    taken[best] = 1;
+  }
+  int i = 0;
+  for (int m = 0; m < M; ++m) {
+    if (!taken[m]) continue;
+    rows[i] = m;
+    float mx = 0.0f;
+    for (int n = 0; n < N; ++n) {
+      float a = fabsf(W[(size_t)m * N + n]);
+      if (a > mx) mx = a;
+    }
+    uint16_t h = or_f32_to_f16((float)((double)mx / 127.0));
+    s_f16[i] = h;
+    double sd = or_f16_to_f64(h);
+    for (int n = 0; n < N; ++n) {
+      int8_t v = 0;
+      if (sd != 0.0) {
+        double r = nearbyint((double)W[(size_t)m * N + n] / sd);
+        if (r > 127.0) r = 127.0;
+        if (r < -127.0) r = -127.0;
+        v = (int8_t)r;
+      }
+      q[(size_t)i * N + n] = v;
+    }
+    for (int k = 0; k < K; ++k) alpha[(size_t)k * M + m] = 0.0f;
+    ++i;
+  }
+  free(taken);
+  free(score);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Physical tile layout (second, independent implementation of the      */
+/* formula documented in include/bsg.h).                               */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The device layout groups the sign words of each base into tiles of 64 rows
+ * by 4 words (128 columns); a tile is stored row-major; tiles follow each
+ * other along the words of a 64-row block, then along the row blocks; the
+ * last row block and the last word group may be narrower.  Each base starts
+ * at a multiple of 64 words.
+ */
+OR_API size_t or_layout_plane_words(int M, int N) {
+  size_t nd = (size_t)(N + 31) / 32;
+  size_t w = (size_t)M * nd;
+  return (w + 63) / 64 * 64;
+}
+
+OR_API size_t or_layout_offset(int K, int M, int N, int k, int m, int w) {
+  (void)K;
+  size_t nd = (size_t)(N + 31) / 32;
+  size_t rb = (size_t)m / 64, r = (size_t)m % 64;
+  size_t h = (size_t)M - rb * 64;
+  if (h > 64) h = 64;
+  size_t g = (size_t)w / 4, j = (size_t)w % 4;
+  size_t wg = nd - g * 4;
+  if (wg > 4) wg = 4;
+  return (size_t)k * or_layout_plane_words(M, N) + rb * 64 * nd + g * 4 * h + r * wg + j;
+}
+
+OR_API void or_logical_to_layout(const uint32_t* logical, int K, int M, int N, uint32_t* phys) {
+  size_t nd = (size_t)(N + 31) / 32;
+  memset(phys, 0, sizeof(uint32_t) * (size_t)K * or_layout_plane_words(M, N));
+  for (int k = 0; k < K; ++k)
+    for (int m = 0; m < M; ++m)
+      for (size_t w = 0; w < nd; ++w)
+        phys[or_layout_offset(K, M, N, k, m, (int)w)] = logical[((size_t)k * M + m) * nd + w];
+}
+
+OR_API void or_layout_to_logical(const uint32_t* phys, int K, int M, int N, uint32_t* logical) {
+  size_t nd = (size_t)(N + 31) / 32;
+  for (int k = 0; k < K; ++k)
+    for (int m = 0; m < M; ++m)
+      for (size_t w = 0; w < nd; ++w)
+        logical[((size_t)k * M + m) * nd + w] = phys[or_layout_offset(K, M, N, k, m, (int)w)];
+}
+
+/* Array forms of the binary16 conversions. */
+OR_API void or_f16_array_to_f64(const uint16_t* h, size_t n, double* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = or_f16_to_f64(h[i]);
+}
+
+OR_API void or_f32_array_to_f16(const float* f, size_t n, uint16_t* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = or_f32_to_f16(f[i]);
+}

@@ -1,0 +1,431 @@
+"""Pins for the CPU oracle: it is checked against what the pages and the
+mathematics fix, never against itself or the HIP path.
+
+Each test names the fact it checks.  A plausible mistake anywhere in the
+oracle (a dropped term, a wrong sign or bit order, a transposed operand, a
+missing residual update) fails at least one of them.
+"""
+import math
+import os
+import re
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_gemv_packed_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    vals = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        k, v = [s.strip() for s in line.split("=", 1)]
+        vals[k] = [float(t) for t in v.split()]
+    return vals
+
+
+def _signs_to_word(signs):
+    w = 0
+    for i, s in enumerate(signs):
+        if s > 0:
+            w |= 1 << i
+    return w
+
+
+def _dense_signs(bits, K, M, N):
+    """+-1 matrices [K][M][N] from logical words, via numpy's little-endian unpackbits."""
+    b = np.asarray(bits, np.uint32).reshape(K, M, -1)
+    by = b.view(np.uint8).reshape(K, M, -1)
+    unpacked = np.unpackbits(by, axis=-1, bitorder="little")[..., :N]
+    return unpacked.astype(np.float64) * 2.0 - 1.0
+
+
+# ----------------------------------------------------------- worked examples
+def test_worked_example_signed_sum():
+    g = _golden("biloco_worked_example.txt")
+    v, x, expect = g["v"], g["x"], g["v.x"][0]
+    word = _signs_to_word(v)
+    assert word == 0b0101
+    y = oracle.sign_gemv(np.array([[[word]]], np.uint32), 1, 1, 4, np.ones((1, 1), np.float32),
+                         np.array(x, np.float64))
+    assert abs(y[0, 0] - expect) <= 1e-12
+    # Same with the input dimension padded to 32: extra columns carry x = 0.
+    xp = np.zeros(32)
+    xp[:4] = x
+    rng = np.random.default_rng(1)
+    wpad = word | (int(rng.integers(0, 2**28)) << 4)
+    y = oracle.sign_gemv(np.array([[[wpad]]], np.uint32), 1, 1, 32, np.ones((1, 1), np.float32), xp)
+    assert abs(y[0, 0] - expect) <= 1e-12
+
+
+def test_worked_example_lowrank_expansion():
+    """alpha * u * (v . x): with alpha = 1 each output is +-3.4 by the sign of u."""
+    g = _golden("biloco_worked_example.txt")
+    v, x, expect = g["v"], g["x"], g["v.x"][0]
+    M, r, N = 37, 32, 4
+    rng = np.random.default_rng(2)
+    u = rng.integers(0, 2, size=M) * 2 - 1
+    ubits = np.zeros((M, 1), np.uint32)
+    ubits[:, 0] = (u > 0).astype(np.uint32)          # rank component 0 only
+    vbits = np.zeros((r, 1), np.uint32)
+    vbits[0, 0] = _signs_to_word(v)
+    alpha_r = np.zeros(r, np.float16)
+    alpha_r[0] = 1.0
+    y = oracle.binlr(ubits, vbits, alpha_r.view(np.uint16), r, M, N, np.array(x))
+    np.testing.assert_allclose(y[:, 0], u * expect, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------- dense equality
+@pytest.mark.parametrize("K,M,N,B,cs", [(1, 5, 7, 1, False), (2, 33, 64, 3, True), (3, 64, 128, 4, True),
+                                        (2, 17, 100, 2, False), (1, 1, 1, 1, True)])
+def test_equals_dense_dequantised_matmul(K, M, N, B, cs):
+    seed = K * 1000 + M * 10 + N
+    bits = synth.random_bits(seed, K, M, N)
+    alpha, csb = synth.random_scales(seed, K, M, N, cs)
+    x = synth.random_x(seed, N, B, "f32")
+    S = _dense_signs(bits, K, M, N)
+    c = np.ones((K, N)) if csb is None else csb.view(np.float16).astype(np.float64)
+    What = np.einsum("km,kmn,kn->mn", alpha.astype(np.float64), S, c)
+    ref = What @ x.astype(np.float64)
+    y = oracle.sign_gemv(bits, K, M, N, alpha, x, csb)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_one_hot_reads_every_bit():
+    K, M, N = 1, 9, 70
+    bits = synth.random_bits(5, K, M, N)
+    alpha, cs = synth.random_scales(5, K, M, N, True)
+    S = _dense_signs(bits, K, M, N)[0]
+    c = cs.view(np.float16).astype(np.float64)[0]
+    for n in range(N):
+        x = np.zeros(N)
+        x[n] = 1.0
+        y = oracle.sign_gemv(bits, K, M, N, alpha, x, cs)[:, 0]
+        np.testing.assert_array_equal(y, alpha[0].astype(np.float64) * c[n] * S[:, n])
+
+
+def test_popcount_closed_form():
+    """x = 1, c = 1, K = 1: y_m = alpha_m * (2 * popcount(row m) - N) exactly."""
+    K, M, N = 1, 50, 96
+    bits = synth.random_bits(6, K, M, N)
+    alpha, _ = synth.random_scales(6, K, M, N, False)
+    y = oracle.sign_gemv(bits, K, M, N, alpha, np.ones(N))[:, 0]
+    for m in range(M):
+        pc = sum(bin(int(w)).count("1") for w in bits[0, m])
+        assert y[m] == float(alpha[0, m]) * (2 * pc - N)
+
+
+def test_negating_all_signs_negates_y():
+    K, M, N, B = 2, 40, 77, 2
+    bits = synth.random_bits(7, K, M, N)
+    alpha, cs = synth.random_scales(7, K, M, N, True)
+    x = synth.random_x(7, N, B, "bf16")
+    y = oracle.sign_gemv(bits, K, M, N, alpha, x, cs)
+    yn = oracle.sign_gemv(~bits, K, M, N, alpha, x, cs)
+    np.testing.assert_array_equal(yn, -y)
+
+
+def test_linearity_small_integers():
+    K, M, N = 2, 20, 64
+    bits = synth.random_bits(8, K, M, N)
+    alpha = np.array([[0.5] * M, [0.25] * M], np.float32)
+    rng = np.random.default_rng(8)
+    x1 = rng.integers(-5, 6, size=N).astype(np.float64)
+    x2 = rng.integers(-5, 6, size=N).astype(np.float64)
+    a = 3.0
+    lhs = oracle.sign_gemv(bits, K, M, N, alpha, a * x1 + x2)
+    rhs = a * oracle.sign_gemv(bits, K, M, N, alpha, x1) + oracle.sign_gemv(bits, K, M, N, alpha, x2)
+    np.testing.assert_array_equal(lhs, rhs)
+
+
+def test_column_permutation_invariance():
+    K, M, N = 1, 12, 64
+    bits = synth.random_bits(9, K, M, N)
+    S = _dense_signs(bits, K, M, N)[0]
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(N)
+    x = rng.integers(-9, 10, size=N).astype(np.float64)
+    pbits = oracle.pack_signs(S[:, perm].astype(np.float32))[None]
+    alpha = np.ones((1, M), np.float32)
+    np.testing.assert_array_equal(oracle.sign_gemv(bits, K, M, N, alpha, x),
+                                  oracle.sign_gemv(pbits, K, M, N, alpha, x[perm]))
+
+
+def test_brute_force_all_patterns_1x8():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal(8)
+    for p in range(256):
+        signs = [1.0 if (p >> i) & 1 else -1.0 for i in range(8)]
+        expect = 0.0
+        for s, xv in zip(signs, x):
+            expect += s * xv
+        y = oracle.sign_gemv(np.array([[[p]]], np.uint32), 1, 1, 8, np.ones((1, 1), np.float32), x)
+        assert abs(y[0, 0] - expect) <= 1e-15 * max(1.0, abs(expect)) * 8
+
+
+# ----------------------------------------------------------- int8 mode
+def test_int8_exact_identity_and_brute_force():
+    K, M, N, B = 2, 30, 96, 3
+    bits = synth.random_bits(11, K, M, N)
+    rng = np.random.default_rng(11)
+    xq = rng.integers(-127, 128, size=(N, B)).astype(np.int8)
+    acc = oracle.sign_gemv_i8(bits, K, M, N, xq)
+    S = _dense_signs(bits, K, M, N)
+    on = (S > 0).astype(np.int64)
+    ident = 2 * np.einsum("kmn,nb->kmb", on, xq.astype(np.int64)) - xq.astype(np.int64).sum(0)[None, None, :]
+    np.testing.assert_array_equal(acc, ident)
+    for k in range(K):
+        for m in (0, M - 1):
+            for b in range(B):
+                s = 0
+                for n in range(N):
+                    s += int(S[k, m, n]) * int(xq[n, b])
+                assert acc[k, m, b] == s
+    assert np.abs(acc).max() < 2**31
+
+
+def test_quantize_i8_rules():
+    x = np.array([127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -127.0, 3.49], np.float32)
+    xq, sx = oracle.quantize_i8(x)
+    assert sx[0] == np.float32(1.0)
+    np.testing.assert_array_equal(xq[:, 0], [127, 0, 2, 2, 0, -2, -127, 3])   # ties to even
+    xq, sx = oracle.quantize_i8(np.zeros(5, np.float32))
+    assert sx[0] == 0 and not xq.any()
+    rng = np.random.default_rng(12)
+    xs = synth.random_x(12, 500, 4, "bf16", "student_t3")
+    xq, sx = oracle.quantize_i8(xs)
+    assert np.abs(xq.astype(int)).max() <= 127
+    for b in range(4):
+        col = xs[:, b]
+        assert abs(int(xq[np.argmax(np.abs(col)), b])) == 127
+        err = np.abs(col.astype(np.float64) - sx[b] * xq[:, b].astype(np.float64))
+        assert err.max() <= 0.5 * sx[b] * (1 + 1e-6)
+        assert np.all((np.sign(xq[:, b]) == np.sign(col)) | (xq[:, b] == 0))
+
+
+# ----------------------------------------------------------- protected rows
+def test_salient_rows_textbook():
+    M, N, ns, B = 40, 64, 5, 2
+    rng = np.random.default_rng(13)
+    rows = np.sort(rng.choice(M, ns, replace=False)).astype(np.int32)
+    q = rng.integers(-127, 128, size=(ns, N)).astype(np.int8)
+    s = rng.uniform(1e-4, 1e-3, size=ns).astype(np.float16)
+    x = synth.random_x(13, N, B, "bf16")
+    y = oracle.salient(rows, q, s.view(np.uint16), M, N, x)
+    ref = np.zeros((M, B))
+    ref[rows] = s.astype(np.float64)[:, None] * (q.astype(np.float64) @ x.astype(np.float64))
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=0)
+
+
+# ----------------------------------------------------------- fp16 conversion
+def test_f16_decode_all_patterns():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f16_to_f64(h)
+    ref = h.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+
+
+def test_f16_encode_matches_ieee_rne():
+    rng = np.random.default_rng(14)
+    vals = [rng.standard_normal(20000).astype(np.float32) * np.float32(s) for s in (1e-8, 1e-6, 1e-4, 1, 100, 6e4)]
+    grid = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+    grid = grid[np.isfinite(grid)]
+    g64 = np.sort(np.unique(grid.astype(np.float64)))
+    mids = ((g64[1:] + g64[:-1]) / 2).astype(np.float32)      # exact ties (representable in fp32)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 65504, 65519.99, 65520, 1e-9, 2.0**-25, 2.0**-24,
+                        3 * 2.0**-26, 2.0**-14, 2.0**-14 * (1 - 2.0**-12)], np.float32)
+    allv = np.concatenate(vals + [grid, mids, special])
+    ours = oracle.f32_to_f16(allv)
+    ref = allv.astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    assert np.isnan(oracle.f32_to_f16(np.array([np.nan], np.float32)).view(np.float16)[0])
+
+
+# ----------------------------------------------------------- packing
+def _residuals_from_outputs(W, bits, alpha, cs, K):
+    """R_k = W - sum_{j<=k} alpha_j c_j s_j, reconstructed in float64 from the outputs."""
+    M, N = W.shape
+    S = _dense_signs(bits, K, M, N)
+    c = np.ones((K, N)) if cs is None else cs.view(np.float16).astype(np.float64)
+    Rs = [W.astype(np.float64)]
+    for k in range(K):
+        Rs.append(Rs[-1] - alpha[k].astype(np.float64)[:, None] * c[k][None, :] * S[k])
+    return Rs, S
+
+
+@pytest.mark.parametrize("K,cs", [(1, False), (2, False), (3, False), (2, True)])
+def test_pack_signs_follow_residual_and_energy_drops(K, cs):
+    M, N = 48, 160
+    W = synth.weights(99, K, M, N)
+    bits, alpha, csb = oracle.pack(W, K, cs)
+    Rs, S = _residuals_from_outputs(W, bits, alpha, csb, K)
+    for k in range(K):
+        # B_k = sign(R_{k-1}), sign(0) = +1
+        np.testing.assert_array_equal(S[k] > 0, Rs[k] >= 0)
+        # alpha_k = mean |R_{k-1}| rounded to fp32
+        np.testing.assert_array_equal(alpha[k], (np.abs(Rs[k]).sum(1) / N).astype(np.float32))
+        e0 = (Rs[k] ** 2).sum(1)
+        e1 = (Rs[k + 1] ** 2).sum(1)
+        assert np.all(e1 < e0)
+        if not cs:
+            # ||R - alpha S||^2 = ||R||^2 - N alpha^2 at alpha = mean|R| (fp32 rounding aside)
+            np.testing.assert_allclose(e1, e0 - N * alpha[k].astype(np.float64) ** 2, rtol=1e-6)
+
+
+def test_pack_alpha_is_fp32_argmin_exact():
+    """Moving alpha by one fp32 ulp either way never lowers the row error (exact rationals)."""
+    M, N = 6, 24
+    W = synth.weights(98, 0, M, N)
+    bits, alpha, _ = oracle.pack(W, 1, False)
+    S = _dense_signs(bits, 1, M, N)[0]
+    for m in range(M):
+        R = [Fraction(float(v)) for v in W[m]]
+        s = [int(v) for v in S[m]]
+
+        def sse(a):
+            a = Fraction(float(a))
+            return sum((r - a * si) ** 2 for r, si in zip(R, s))
+
+        a0 = alpha[0, m]
+        base = sse(a0)
+        for d in (np.inf, -np.inf):
+            assert sse(np.nextafter(a0, np.float32(d))) >= base
+
+
+def test_pack_colscale_is_fp16_argmin_exact():
+    """Parity unpinned by page values; pinned by least-squares optimality:
+    each column scale is the fp16 value minimising the column error given alpha and B."""
+    M, N = 10, 40
+    W = synth.weights(97, 0, M, N)
+    bits, alpha, cs = oracle.pack(W, 1, True)
+    S = _dense_signs(bits, 1, M, N)[0]
+    c16 = cs[0].view(np.float16)
+    for n in range(N):
+        R = [Fraction(float(W[m, n])) for m in range(M)]
+        a = [Fraction(float(alpha[0, m])) for m in range(M)]
+
+        def sse(c):
+            c = Fraction(float(c))
+            return sum((R[m] - a[m] * c * int(S[m, n])) ** 2 for m in range(M))
+
+        base = sse(c16[n])
+        for d in (np.inf, -np.inf):
+            assert sse(np.nextafter(c16[n], np.float16(d))) >= base
+
+
+def test_pack_zero_maps_to_plus_one():
+    W = np.array([[0.0, -0.0, -1.0, 2.0]], np.float32)
+    bits, alpha, _ = oracle.pack(W, 1, False)
+    assert int(bits[0, 0, 0]) == 0b1011
+    assert alpha[0, 0] == np.float32(0.75)
+
+
+def test_pack_signs_helper():
+    S = np.array([[1, -1, 0, -0.0, -3]], np.float32)
+    assert int(oracle.pack_signs(S)[0, 0]) == 0b01101
+
+
+# ----------------------------------------------------------- protected-row selection
+def test_salient_select_rules():
+    """Parity unpinned by page values; pinned by the selection definition:
+    top-ns rows by sum_n |W| xbar, ties to the smaller row, symmetric int8."""
+    M, N, ns, K = 60, 48, 7, 2
+    W = synth.weights(96, 0, M, N)
+    W[10] = W[3]        # a tie: rows 3 and 10 have identical scores
+    W[3] *= 4
+    W[10] *= 4
+    xbar = np.abs(synth.random_x(96, N, 1, "f32"))[:, 0].astype(np.float32)
+    alpha = np.ones((K, M), np.float32)
+    rows, q, s, a = oracle.salient_select(W, xbar, ns, alpha)
+    score = np.abs(W.astype(np.float64)) @ xbar.astype(np.float64)
+    order = sorted(range(M), key=lambda m: (-score[m], m))
+    assert list(rows) == sorted(order[:ns])
+    assert 3 in rows and 10 in rows
+    sd = s.view(np.float16).astype(np.float64)
+    for i, m in enumerate(rows):
+        mx = np.abs(W[m]).max()
+        assert s[i] == np.float32(np.float64(mx) / 127).astype(np.float16).view(np.uint16)
+        assert np.abs(q[i].astype(int)).max() <= 127
+        err = np.abs(W[m].astype(np.float64) - sd[i] * q[i])
+        clip = np.abs(W[m].astype(np.float64) / sd[i]) > 127
+        assert np.all(err[~clip] <= 0.5 * sd[i] * (1 + 1e-12))
+    kept = np.zeros(M, bool)
+    kept[rows] = True
+    assert np.all(a[:, kept] == 0) and np.all(a[:, ~kept] == 1)
+    # the smaller index wins a tie at the cut
+    W2 = np.zeros((4, 8), np.float32)
+    W2[:] = 1.0
+    rows2, _, _, _ = oracle.salient_select(W2, np.ones(8, np.float32), 2)
+    assert list(rows2) == [0, 1]
+
+
+def test_absmean():
+    X = synth.calibration(synth.WORKLOADS[5], 0, 300, 128)
+    ours = oracle.absmean(X)
+    ref = np.abs(X.astype(np.float64)).mean(0).astype(np.float32)
+    np.testing.assert_allclose(ours, ref, rtol=2e-7, atol=0)
+
+
+# ----------------------------------------------------------- layout
+@pytest.mark.parametrize("K,M,N", [(1, 64, 128), (2, 70, 160), (3, 130, 32), (1, 1, 96), (2, 200, 544)])
+def test_layout_is_a_bijection_and_tiles_are_row_major(K, M, N):
+    nd = oracle.words(N)
+    total = oracle.layout_words(K, M, N)
+    plane = total // K
+    assert plane % 64 == 0 and plane >= M * nd
+    seen = set()
+    for k in range(K):
+        for m in range(M):
+            for w in range(nd):
+                o = oracle.layout_offset(K, M, N, k, m, w)
+                assert k * plane <= o < k * plane + M * nd
+                seen.add(o)
+    assert len(seen) == K * M * nd
+    # a full tile (64 rows x 4 words) is one contiguous row-major block of 256 words
+    if M >= 64 and nd >= 4:
+        base = oracle.layout_offset(K, M, N, 0, 0, 0)
+        for m in range(64):
+            for w in range(4):
+                assert oracle.layout_offset(K, M, N, 0, m, w) == base + m * 4 + w
+    L = synth.random_bits(K * M + N, K, M, N)
+    np.testing.assert_array_equal(oracle.from_layout(oracle.to_layout(L, K, M, N), K, M, N), L)
+
+
+# ----------------------------------------------------------- storage arithmetic
+def test_storage_arithmetic_5120_rank512():
+    g = _golden("biloco_storage.txt")
+    M, N = [int(v) for v in g["matrix"]]
+    r_bin, r_bf16 = int(g["binary_rank"][0]), int(g["bf16_rank"][0])
+    u = np.ones((M, r_bin), np.float32)
+    v = np.ones((r_bin, N), np.float32)
+    bits = oracle.pack_signs(u).nbytes * 8 + oracle.pack_signs(v).nbytes * 8
+    assert bits == 2 * 5120 * 512 == 5_242_880
+    assert bits == 2 * M * r_bf16 * 16                         # same storage as BF16 rank 32
+    assert abs(bits / 1e6 - g["both_corrections_mbit_approx"][0]) < 0.05
+    assert r_bin // r_bf16 == g["rank_ratio_same_storage"][0]
+    fp4_bits = M * N * 4.5                                   # 4 bits + one FP8 scale per 16 values
+    assert abs(fp4_bits / 1e6 - g["fp4_weight_mbit_approx"][0]) / g["fp4_weight_mbit_approx"][0] < 0.03
+    assert round(100 * bits / fp4_bits) == g["overhead_percent_approx"][0]
+    r128 = oracle.pack_signs(np.ones((M, 128), np.float32)).nbytes + oracle.pack_signs(np.ones((128, N), np.float32)).nbytes
+    assert r128 == 163_840
+    assert abs(r128 / 2**20 - g["rank128_sign_bits_mib_approx"][0]) < 0.005
+    fp4_bytes = M * N * 4 // 8
+    assert fp4_bytes / 2**20 == g["fp4_weights_mib_approx"][0]
+    assert round(fp4_bytes / r128) == g["read_ratio_approx"][0]
+
+
+def test_tolerance_reduces_to_row_bound():
+    K, M, N = 2, 8, 64
+    alpha, _ = synth.random_scales(3, K, M, N, False)
+    x = synth.random_x(3, N, 1, "bf16")
+    t = oracle.tolerance(x, alpha=alpha)
+    ref = 2e-3 * np.abs(alpha.astype(np.float64)).sum(0) * np.abs(x).sum()
+    np.testing.assert_allclose(t[:, 0], ref, rtol=1e-12)
