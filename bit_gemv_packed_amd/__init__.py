@@ -1,0 +1,314 @@
+"""bit_gemv_packed_amd -- binary sign-GEMV for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over libbsg.so (the C ABI in include/bsg.h).  Every
+function marshals torch tensors into device pointers and the current HIP
+stream and calls the entry point of the same name; all arithmetic runs in
+the library's HIP kernels.  There is no CPU fallback: if libbsg.so is
+missing, or a tensor is not on the GPU, the call raises.
+
+The page passages each operation follows are cited in include/bsg.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsg.so")
+
+BSG_F32, BSG_F16, BSG_BF16 = 0, 1, 2
+BSG_PACK_COLSCALE = 1
+
+_STATUS_NAMES = {0: "BSG_OK", -1: "BSG_ERR_NULL", -2: "BSG_ERR_SHAPE", -3: "BSG_ERR_DTYPE",
+                 -4: "BSG_ERR_ALIGN", -5: "BSG_ERR_UNSUPPORTED", -6: "BSG_ERR_WORKSPACE", -7: "BSG_ERR_HIP"}
+
+
+class BsgError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__("%s failed: %s (%d: %s)" % (fn, _STATUS_NAMES.get(status, "?"), status, message))
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "bsg_abi_version": (ctypes.c_int32, []),
+    "bsg_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+    "bsg_layout_words": (_SZ, [_I, _I, _I]),
+    "bsg_layout_word_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
+    "bsg_gemv_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "bsg_binlr_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "bsq_pack_workspace_bytes": (_SZ, [_I, _I]),
+    "bsq_salient_workspace_bytes": (_SZ, [_I, _I]),
+    "bsq_pack": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "bsq_pack_signs": (ctypes.c_int32, [_P, _I, _I, _P, _P]),
+    "bsq_absmean": (ctypes.c_int32, [_P, _I, _I, _P, _P]),
+    "bsq_salient": (ctypes.c_int32, [_P, _I, _I, _P, _I, _P, _P, _P, _P, _I, _P, _SZ, _P]),
+    "bsq_quantize_i8": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P]),
+    "bsg_logical_to_layout": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P]),
+    "bsg_layout_to_logical": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P]),
+    "bs_gemv": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, _SZ, _P]),
+    "bs_gemv_i8": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _I, _P, _SZ, _P]),
+    "binlr_apply": (ctypes.c_int32, [_P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P, _SZ, _P]),
+    "salient_int8_apply": (ctypes.c_int32, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _P]),
+}
+
+
+def lib():
+    """Load libbsg.so (built in-tree by bit_gemv_packed_amd.build).  Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libbsg.so is not built (%s); run bit_gemv_packed_amd.build.build() "
+                              "or __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().bsg_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise BsgError(fn, status, status_string(status))
+
+
+# ------------------------------------------------------------------ helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU (device %s given)" % t.device)
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device=None) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return BSG_F32
+    if t.dtype == torch.float16:
+        return BSG_F16
+    if t.dtype == torch.bfloat16:
+        return BSG_BF16
+    raise TypeError("unsupported activation dtype %s" % t.dtype)
+
+
+def _xshape(x, N: int) -> int:
+    if x.dim() == 1:
+        if x.shape[0] != N:
+            raise ValueError("x must have N=%d elements" % N)
+        return 1
+    if x.dim() != 2 or x.shape[0] != N:
+        raise ValueError("x must be [N][B] with N=%d" % N)
+    return x.shape[1]
+
+
+def zeros_workspace(nbytes: int, device) -> Optional["object"]:
+    """A zero-filled device workspace of nbytes (None when nbytes == 0)."""
+    if nbytes == 0:
+        return None
+    torch = _torch()
+    return torch.zeros((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+class Workspace:
+    """Per-device cache of zero-filled workspaces, reused across calls on one
+    stream (every completed call leaves its workspace zero-filled)."""
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, nbytes: int, device):
+        if nbytes == 0:
+            return None
+        key = (str(device), "ws")
+        buf = self._bufs.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = zeros_workspace(max(nbytes, 1 << 20), device)
+            self._bufs[key] = buf
+        return buf
+
+
+_WS = Workspace()
+
+
+def _ws_args(ws):
+    if ws is None:
+        return None, 0
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+# ------------------------------------------------------------------ sizes
+def layout_words(K: int, M: int, N: int) -> int:
+    return int(lib().bsg_layout_words(K, M, N))
+
+
+def layout_word_offset(K: int, M: int, N: int, k: int, m: int, w: int) -> int:
+    return int(lib().bsg_layout_word_offset(K, M, N, k, m, w))
+
+
+def gemv_workspace_bytes(K: int, M: int, N: int, B: int) -> int:
+    return int(lib().bsg_gemv_workspace_bytes(K, M, N, B))
+
+
+def binlr_workspace_bytes(r: int, M: int, N: int, B: int) -> int:
+    return int(lib().bsg_binlr_workspace_bytes(r, M, N, B))
+
+
+# ------------------------------------------------------------------ packing
+def bsq_pack(W, K: int, colscale: bool = False, workspace=None):
+    """Greedy residual binary bases of W (fp32 [M][N] on the GPU).
+    Returns (bits int32 [layout words], alpha fp32 [K][M], colscale fp16-bits int16 [K][N] or None)."""
+    torch = _torch()
+    M, N = W.shape
+    dev = W.device
+    bits = torch.empty(layout_words(K, M, N), dtype=torch.int32, device=dev)
+    alpha = torch.empty((K, M), dtype=torch.float32, device=dev)
+    cs = torch.empty((K, N), dtype=torch.int16, device=dev) if colscale else None
+    nb = int(lib().bsq_pack_workspace_bytes(M, N))
+    ws = workspace if workspace is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
+    _check("bsq_pack", lib().bsq_pack(_ptr(W), M, N, K, BSG_PACK_COLSCALE if colscale else 0, _ptr(bits),
+                                      _ptr(alpha), _ptr(cs), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return bits, alpha, cs
+
+
+def bsq_pack_signs(S):
+    """Device sign layout (K = 1) of a real matrix S (fp32 [M][N] on the GPU): bit = [S >= 0]."""
+    torch = _torch()
+    M, N = S.shape
+    bits = torch.empty(layout_words(1, M, N), dtype=torch.int32, device=S.device)
+    _check("bsq_pack_signs", lib().bsq_pack_signs(_ptr(S), M, N, _ptr(bits), _stream(S.device)))
+    return bits
+
+
+def bsq_absmean(X):
+    torch = _torch()
+    S, N = X.shape
+    xbar = torch.empty(N, dtype=torch.float32, device=X.device)
+    _check("bsq_absmean", lib().bsq_absmean(_ptr(X), S, N, _ptr(xbar), _stream(X.device)))
+    return xbar
+
+
+def bsq_salient(W, xbar, ns: int, alpha=None):
+    """Protected int8 rows.  Returns (rows int32 [ns], q int8 [ns][N], s fp16-bits int16 [ns]);
+    alpha (fp32 [K][M]) is updated in place (kept rows zeroed)."""
+    torch = _torch()
+    M, N = W.shape
+    dev = W.device
+    rows = torch.empty(max(ns, 1), dtype=torch.int32, device=dev)[:ns]
+    q = torch.empty((max(ns, 1), N), dtype=torch.int8, device=dev)[:ns]
+    s = torch.empty(max(ns, 1), dtype=torch.int16, device=dev)[:ns]
+    K = 0 if alpha is None else alpha.shape[0]
+    nb = int(lib().bsq_salient_workspace_bytes(M, N))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    _check("bsq_salient", lib().bsq_salient(_ptr(W), M, N, _ptr(xbar), ns, rows.data_ptr(), q.data_ptr(),
+                                            s.data_ptr(), _ptr(alpha), K, ws.data_ptr(), nb, _stream(dev)))
+    return rows, q, s
+
+
+def bsq_quantize_i8(x):
+    torch = _torch()
+    N = x.shape[0]
+    B = _xshape(x, N)
+    xq = torch.empty((N, B), dtype=torch.int8, device=x.device)
+    sx = torch.empty(B, dtype=torch.float32, device=x.device)
+    _check("bsq_quantize_i8", lib().bsq_quantize_i8(_ptr(x), _dtype_code(x), N, B, _ptr(xq), _ptr(sx),
+                                                    _stream(x.device)))
+    return xq, sx
+
+
+def bsg_logical_to_layout(logical, K: int, M: int, N: int):
+    torch = _torch()
+    bits = torch.zeros(layout_words(K, M, N), dtype=torch.int32, device=logical.device)
+    _check("bsg_logical_to_layout", lib().bsg_logical_to_layout(_ptr(logical), K, M, N, _ptr(bits),
+                                                                _stream(logical.device)))
+    return bits
+
+
+def bsg_layout_to_logical(bits, K: int, M: int, N: int):
+    torch = _torch()
+    logical = torch.empty((K, M, N // 32), dtype=torch.int32, device=bits.device)
+    _check("bsg_layout_to_logical", lib().bsg_layout_to_logical(_ptr(bits), K, M, N, _ptr(logical),
+                                                                _stream(bits.device)))
+    return logical
+
+
+# ------------------------------------------------------------------ hot path
+def bs_gemv(bits, K: int, M: int, N: int, alpha, x, colscale=None, y=None, accumulate: bool = False,
+            workspace=None):
+    """y (fp32 [M][B]) = or += sum_k alpha_k (.) (B_k (c_k (.) x)).  x: [N] or [N][B]."""
+    torch = _torch()
+    B = _xshape(x, N)
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, B), dtype=torch.float32, device=dev)
+    nb = gemv_workspace_bytes(K, M, N, B)
+    ws = workspace if workspace is not None else _WS.get(nb, dev)
+    wp, wn = _ws_args(ws)
+    _check("bs_gemv", lib().bs_gemv(_ptr(bits), K, M, N, _ptr(alpha), _ptr(colscale), _ptr(x), _dtype_code(x), B,
+                                    _ptr(y), 1 if accumulate else 0, wp, wn, _stream(dev)))
+    return y
+
+
+def bs_gemv_i8(bits, K: int, M: int, N: int, alpha, xq, sx, want_acc: bool = True, want_y: bool = True,
+               y=None, accumulate: bool = False, workspace=None) -> Tuple[Optional[object], Optional[object]]:
+    """Exact int8-activation product.  Returns (acc int32 [K][M][B] or None, y fp32 [M][B] or None)."""
+    torch = _torch()
+    B = _xshape(xq, N)
+    dev = xq.device
+    acc = torch.empty((K, M, B), dtype=torch.int32, device=dev) if want_acc else None
+    if want_y and y is None:
+        y = torch.empty((M, B), dtype=torch.float32, device=dev)
+    if not want_y:
+        y = None
+    nb = gemv_workspace_bytes(K, M, N, B)
+    ws = workspace if workspace is not None else _WS.get(nb, dev)
+    wp, wn = _ws_args(ws)
+    _check("bs_gemv_i8", lib().bs_gemv_i8(_ptr(bits), K, M, N, _ptr(alpha), _ptr(xq), _ptr(sx), B, _ptr(acc),
+                                          _ptr(y), 1 if accumulate else 0, wp, wn, _stream(dev)))
+    return acc, y
+
+
+def binlr_apply(U_bits, V_bits, alpha_r, r: int, M: int, N: int, x, y, workspace=None):
+    """y += sum_j su(:, j) * alpha_r[j] * (sv(j, :) . x)  (binary low-rank correction)."""
+    B = _xshape(x, N)
+    dev = x.device
+    nb = binlr_workspace_bytes(r, M, N, B)
+    ws = workspace if workspace is not None else _WS.get(nb, dev)
+    wp, wn = _ws_args(ws)
+    _check("binlr_apply", lib().binlr_apply(_ptr(U_bits), _ptr(V_bits), _ptr(alpha_r), r, M, N, _ptr(x),
+                                            _dtype_code(x), B, _ptr(y), wp, wn, _stream(dev)))
+    return y
+
+
+def salient_int8_apply(rows, q, s, M: int, N: int, x, y):
+    """y[rows[i]] += s_i * (q[i] . x)  (protected int8 rows)."""
+    B = _xshape(x, N)
+    ns = rows.numel()
+    if ns == 0:
+        return y
+    _check("salient_int8_apply", lib().salient_int8_apply(_ptr(rows), ns, _ptr(q), _ptr(s), M, N, _ptr(x),
+                                                          _dtype_code(x), B, _ptr(y), _stream(x.device)))
+    return y

@@ -1,0 +1,299 @@
+// C ABI of libbsg: host-side argument validation, launch planning and
+// dispatch.  Validation is a pure function of the arguments (no device
+// pointer is dereferenced) and runs before any HIP call.
+#include <cstdint>
+#include <cstdlib>
+
+#include "bsg_internal.h"
+
+namespace bsg {
+hipError_t launch_pack(const float* W, int M, int N, int K, bool colscale, uint32_t* bits, float* alpha,
+                       uint16_t* cs, void* ws, hipStream_t st);
+hipError_t launch_pack_signs(const float* S, int M, int N, uint32_t* bits, hipStream_t st);
+hipError_t launch_absmean(const float* X, int S, int N, float* xbar, hipStream_t st);
+hipError_t launch_salient(const float* W, int M, int N, const float* xbar, int ns, int32_t* rows, int8_t* q,
+                          uint16_t* s, float* alpha, int K, void* ws, hipStream_t st);
+hipError_t launch_salient_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s, int M, int N,
+                                const void* x, int xdt, int B, float* y, hipStream_t st);
+hipError_t launch_quantize(const void* x, int xdt, int N, int B, int8_t* xq, float* sx, hipStream_t st);
+hipError_t launch_layout(const uint32_t* src, int K, int M, int N, uint32_t* dst, bool to_layout, hipStream_t st);
+}  // namespace bsg
+
+using namespace bsg;
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+bool misaligned(const void* p, size_t a) { return p && (((uintptr_t)p) % a) != 0; }
+
+bool bad_dtype(int dt) { return dt != BSG_F32 && dt != BSG_F16 && dt != BSG_BF16; }
+
+size_t dtype_size(int dt) { return dt == BSG_F32 ? 4 : 2; }
+
+bool bad_n(int N) { return N <= 0 || (N % 32) != 0; }
+
+bsg_status hip_status(hipError_t e) { return e == hipSuccess ? BSG_OK : BSG_ERR_HIP; }
+
+// binlr workspace: [counters][z fp32 [r][B]][partials of whichever pass needs more]
+size_t binlr_ws(int r, int M, int N, int B) {
+  const GemvPlan pv = plan_gemv(1, r, N, B, false);
+  const GemvPlan pu = plan_gemv(1, M, r, B, false);
+  const size_t part = pv.part_bytes > pu.part_bytes ? pv.part_bytes : pu.part_bytes;
+  return kCounterBytes + align_up((size_t)r * B * 4, 256) + part;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bsg_abi_version(void) { return kAbiVersion; }
+
+const char* bsg_status_string(bsg_status s) {
+  switch (s) {
+    case BSG_OK: return "ok";
+    case BSG_ERR_NULL: return "a required pointer is NULL";
+    case BSG_ERR_SHAPE: return "invalid size (negative, N not a multiple of 32, or count out of range)";
+    case BSG_ERR_DTYPE: return "unknown dtype";
+    case BSG_ERR_ALIGN: return "misaligned device pointer";
+    case BSG_ERR_UNSUPPORTED: return "unsupported combination";
+    case BSG_ERR_WORKSPACE: return "workspace missing or too small";
+    case BSG_ERR_HIP: return "HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t bsg_layout_words(int K, int M, int N) {
+  if (K < 1 || M < 0 || bad_n(N)) return 0;
+  return (size_t)K * plane_words(M, N / 32);
+}
+
+int64_t bsg_layout_word_offset(int K, int M, int N, int k, int m, int w) {
+  if (K < 1 || M < 0 || bad_n(N)) return -1;
+  if (k < 0 || k >= K || m < 0 || m >= M || w < 0 || w >= N / 32) return -1;
+  return (int64_t)layout_offset(M, N / 32, plane_words(M, N / 32), k, m, w);
+}
+
+size_t bsg_gemv_workspace_bytes(int K, int M, int N, int B) {
+  if (K < 1 || K > kMaxK || M <= 0 || bad_n(N) || B < 1 || B > kMaxB) return 0;
+  const GemvPlan pf = plan_gemv(K, M, N, B, false);
+  const GemvPlan pi = plan_gemv(K, M, N, B, true);
+  return pf.ws_bytes > pi.ws_bytes ? pf.ws_bytes : pi.ws_bytes;
+}
+
+size_t bsg_binlr_workspace_bytes(int r, int M, int N, int B) {
+  if (r <= 0 || (r % 32) != 0 || M < 0 || bad_n(N) || B < 1 || B > kMaxB) return 0;
+  return binlr_ws(r, M > 0 ? M : 1, N, B);
+}
+
+size_t bsq_pack_workspace_bytes(int M, int N) {
+  if (M < 0 || bad_n(N)) return 0;
+  return align_up((size_t)M * N * 8, 256) + 256;
+}
+
+size_t bsq_salient_workspace_bytes(int M, int N) {
+  if (M < 0 || N <= 0) return 0;
+  return align_up((size_t)M * 8, 256) + align_up((size_t)M * 4, 256);
+}
+
+bsg_status bsq_pack(const float* W, int M, int N, int K, int flags, uint32_t* bits, float* alpha,
+                    uint16_t* colscale, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool cs = (flags & BSG_PACK_COLSCALE) != 0;
+  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || (flags & ~BSG_PACK_COLSCALE)) return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!W || !bits || !alpha || (cs && !colscale)) return BSG_ERR_NULL;
+  if (misaligned(W, 4) || misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(colscale, 2) ||
+      misaligned(workspace, 16))
+    return BSG_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bsq_pack_workspace_bytes(M, N)) return BSG_ERR_WORKSPACE;
+  return hip_status(launch_pack(W, M, N, K, cs, bits, alpha, cs ? colscale : nullptr, workspace,
+                                (hipStream_t)stream));
+}
+
+bsg_status bsq_pack_signs(const float* S, int M, int N, uint32_t* bits, void* stream) {
+  if (M < 0 || bad_n(N)) return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!S || !bits) return BSG_ERR_NULL;
+  if (misaligned(S, 4) || misaligned(bits, 16)) return BSG_ERR_ALIGN;
+  return hip_status(launch_pack_signs(S, M, N, bits, (hipStream_t)stream));
+}
+
+bsg_status bsq_absmean(const float* X, int S, int N, float* xbar, void* stream) {
+  if (S < 1 || N <= 0) return BSG_ERR_SHAPE;
+  if (!X || !xbar) return BSG_ERR_NULL;
+  if (misaligned(X, 4) || misaligned(xbar, 4)) return BSG_ERR_ALIGN;
+  return hip_status(launch_absmean(X, S, N, xbar, (hipStream_t)stream));
+}
+
+bsg_status bsq_salient(const float* W, int M, int N, const float* xbar, int ns, int32_t* rows, int8_t* q,
+                       uint16_t* s_f16, float* alpha, int K, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (M < 0 || N <= 0 || ns < 0 || ns > M || K < 0 || K > kMaxK) return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!W || !xbar || (ns > 0 && (!rows || !q || !s_f16)) || (K > 0 && !alpha)) return BSG_ERR_NULL;
+  if (misaligned(W, 4) || misaligned(xbar, 4) || misaligned(rows, 4) || misaligned(s_f16, 2) ||
+      misaligned(alpha, 4) || misaligned(workspace, 16))
+    return BSG_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bsq_salient_workspace_bytes(M, N)) return BSG_ERR_WORKSPACE;
+  return hip_status(launch_salient(W, M, N, xbar, ns, rows, q, s_f16, alpha, K, workspace, (hipStream_t)stream));
+}
+
+bsg_status bsq_quantize_i8(const void* x, int x_dtype, int N, int B, int8_t* xq, float* sx, void* stream) {
+  if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
+  if (N <= 0 || B < 1) return BSG_ERR_SHAPE;
+  if (!x || !xq || !sx) return BSG_ERR_NULL;
+  if (misaligned(x, dtype_size(x_dtype)) || misaligned(sx, 4)) return BSG_ERR_ALIGN;
+  return hip_status(launch_quantize(x, x_dtype, N, B, xq, sx, (hipStream_t)stream));
+}
+
+bsg_status bsg_logical_to_layout(const uint32_t* logical, int K, int M, int N, uint32_t* bits, void* stream) {
+  if (K < 1 || M < 0 || bad_n(N)) return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!logical || !bits) return BSG_ERR_NULL;
+  if (misaligned(logical, 4) || misaligned(bits, 16)) return BSG_ERR_ALIGN;
+  return hip_status(launch_layout(logical, K, M, N, bits, true, (hipStream_t)stream));
+}
+
+bsg_status bsg_layout_to_logical(const uint32_t* bits, int K, int M, int N, uint32_t* logical, void* stream) {
+  if (K < 1 || M < 0 || bad_n(N)) return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!logical || !bits) return BSG_ERR_NULL;
+  if (misaligned(logical, 4) || misaligned(bits, 16)) return BSG_ERR_ALIGN;
+  return hip_status(launch_layout(bits, K, M, N, logical, false, (hipStream_t)stream));
+}
+
+bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const float* alpha, const uint16_t* colscale,
+                   const void* x, int x_dtype, int B, float* y, int accumulate, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
+  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || B < 1 || B > kMaxB) return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!bits || !alpha || !x || !y) return BSG_ERR_NULL;
+  if (misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(colscale, 2) ||
+      misaligned(x, dtype_size(x_dtype)) || misaligned(y, 4) || misaligned(workspace, 16))
+    return BSG_ERR_ALIGN;
+  const GemvPlan p = plan_gemv(K, M, N, B, false);
+  if (p.ws_bytes && (!workspace || workspace_bytes < p.ws_bytes)) return BSG_ERR_WORKSPACE;
+  GemvArgs a{};
+  a.bits = bits;
+  a.alpha = alpha;
+  a.colscale = colscale;
+  a.x = x;
+  a.y = y;
+  a.cnt = p.ws_bytes ? (unsigned*)workspace : nullptr;
+  a.part = p.ws_bytes ? (float*)((char*)workspace + kCounterBytes) : nullptr;
+  a.plane = plane_words(M, N / 32);
+  a.K = K;
+  a.M = M;
+  a.N = N;
+  a.ND = N / 32;
+  a.B = B;
+  a.xdt = x_dtype;
+  a.accumulate = accumulate ? 1 : 0;
+  a.S = p.S;
+  a.wb = p.wb;
+  return hip_status(launch_gemv_f(a, p, (hipStream_t)stream));
+}
+
+bsg_status bs_gemv_i8(const uint32_t* bits, int K, int M, int N, const float* alpha, const int8_t* xq,
+                      const float* sx, int B, int32_t* acc, float* y, int accumulate, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || N > (1 << 24) || B < 1 || B > kMaxB) return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!bits || !xq || (!acc && !y) || (y && (!alpha || !sx))) return BSG_ERR_NULL;
+  if (misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(sx, 4) || misaligned(acc, 4) ||
+      misaligned(y, 4) || misaligned(workspace, 16))
+    return BSG_ERR_ALIGN;
+  const GemvPlan p = plan_gemv(K, M, N, B, true);
+  if (p.ws_bytes && (!workspace || workspace_bytes < p.ws_bytes)) return BSG_ERR_WORKSPACE;
+  GemvI8Args a{};
+  a.bits = bits;
+  a.alpha = alpha;
+  a.xq = xq;
+  a.sx = sx;
+  a.acc = acc;
+  a.y = y;
+  a.cnt = p.ws_bytes ? (unsigned*)workspace : nullptr;
+  a.part = p.ws_bytes ? (int32_t*)((char*)workspace + kCounterBytes) : nullptr;
+  a.plane = plane_words(M, N / 32);
+  a.K = K;
+  a.M = M;
+  a.N = N;
+  a.ND = N / 32;
+  a.B = B;
+  a.accumulate = accumulate ? 1 : 0;
+  a.S = p.S;
+  a.wb = p.wb;
+  return hip_status(launch_gemv_i8(a, p, (hipStream_t)stream));
+}
+
+bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uint16_t* alpha_r, int r, int M,
+                       int N, const void* x, int x_dtype, int B, float* y, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
+  if (r <= 0 || (r % 32) != 0 || M < 0 || bad_n(N) || B < 1 || B > kMaxB) return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!U_bits || !V_bits || !alpha_r || !x || !y) return BSG_ERR_NULL;
+  if (misaligned(U_bits, 16) || misaligned(V_bits, 16) || misaligned(alpha_r, 2) ||
+      misaligned(x, dtype_size(x_dtype)) || misaligned(y, 4) || misaligned(workspace, 16))
+    return BSG_ERR_ALIGN;
+  if (!workspace || workspace_bytes < binlr_ws(r, M, N, B)) return BSG_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const GemvPlan pv = plan_gemv(1, r, N, B, false);
+  const GemvPlan pu = plan_gemv(1, M, r, B, false);
+  char* ws = (char*)workspace;
+  unsigned* cnt = (unsigned*)ws;
+  float* z = (float*)(ws + kCounterBytes);
+  float* part = (float*)(ws + kCounterBytes + align_up((size_t)r * B * 4, 256));
+
+  GemvArgs v{};
+  v.bits = V_bits;
+  v.alpha_h = alpha_r;
+  v.x = x;
+  v.y = z;
+  v.part = part;
+  v.cnt = cnt;
+  v.plane = plane_words(r, N / 32);
+  v.K = 1;
+  v.M = r;
+  v.N = N;
+  v.ND = N / 32;
+  v.B = B;
+  v.xdt = x_dtype;
+  v.accumulate = 0;
+  v.S = pv.S;
+  v.wb = pv.wb;
+  hipError_t e = launch_gemv_f(v, pv, st);
+  if (e != hipSuccess) return BSG_ERR_HIP;
+
+  GemvArgs u{};
+  u.bits = U_bits;
+  u.x = z;
+  u.y = y;
+  u.part = part;
+  u.cnt = cnt;
+  u.plane = plane_words(M, r / 32);
+  u.K = 1;
+  u.M = M;
+  u.N = r;
+  u.ND = r / 32;
+  u.B = B;
+  u.xdt = BSG_F32;
+  u.accumulate = 1;
+  u.S = pu.S;
+  u.wb = pu.wb;
+  return hip_status(launch_gemv_f(u, pu, st));
+}
+
+bsg_status salient_int8_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s_f16, int M, int N,
+                              const void* x, int x_dtype, int B, float* y, void* stream) {
+  if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
+  if (ns < 0 || M < 0 || N <= 0 || B < 1 || B > kMaxB) return BSG_ERR_SHAPE;
+  if (M == 0 || ns == 0) return BSG_OK;
+  if (!rows || !q || !s_f16 || !x || !y) return BSG_ERR_NULL;
+  if (misaligned(rows, 4) || misaligned(s_f16, 2) || misaligned(x, dtype_size(x_dtype)) || misaligned(y, 4))
+    return BSG_ERR_ALIGN;
+  return hip_status(launch_salient_apply(rows, ns, q, s_f16, M, N, x, x_dtype, B, y, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,265 @@
+/*
+ * bsg.h -- C ABI of libbsg, the binary sign-GEMV library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The decode-time product with binary-compressed weights
+ *
+ *     y = sum_k alpha_k (.) (B_k (c_k (.) x))                  binary bases
+ *       + sum_j alpha_r[j] * u_j * (v_j . x)                     low-rank signs
+ *       + (protected int8 rows)
+ *
+ * Sources (the web pages this library is built from):
+ *  - "FluxBin: Flexible LUT-based Ultra-low-bit LLM Inference by
+ *    Algorithm-Kernel Synergy": Sec. 2 (weights approximated by a greedy
+ *    residual sum of binary bases), Sec. 3.1 (decoupled row and column scales;
+ *    the quantised matrix is the sum over bases), Sec. 3.2 Stage 1 (a set bit b
+ *    means +1 and a clear bit -1, i.e. 2b-1; the column scale is folded into
+ *    the activation before the main loop).
+ *  - "BiLoCo: Binary Low-Rank Corrections for Post-Training Quantization":
+ *    "The core idea" (correction alpha*u*(v.x) with u, v in {+1,-1}, computed
+ *    with additions and subtractions only).
+ *  - "BiSCo-LLM: Lookup-Free Binary Spherical Coding for Extreme Low-Bit LLM
+ *    Compression", technical summary, "Sensitivity Protection" (about 1% of
+ *    sensitive channels, chosen from activation statistics and weight
+ *    magnitudes, kept in 8 bits apart from the binary payload).
+ *
+ * General rules for every entry point:
+ *  - Pointers marked (device) are device memory of the current HIP device;
+ *    (host) pointers are host memory.  Every buffer is owned by the caller;
+ *    the library allocates no device memory and keeps no state between calls
+ *    other than its loaded code objects.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL means
+ *    the null stream).  No entry point synchronises.  Asynchronous faults
+ *    surface at the caller's next synchronisation.
+ *  - Arguments are validated on the host before any HIP call; a non-zero
+ *    return means nothing was enqueued (except BSG_ERR_HIP, reported when a
+ *    launch fails).  Validation never dereferences device pointers.
+ *  - Sign buffers and workspaces must be 16-byte aligned; every other
+ *    pointer must be aligned to its element size (BSG_ERR_ALIGN).
+ *  - N (the input dimension) must be a positive multiple of 32; M >= 0; an
+ *    M of 0 is a no-op returning BSG_OK.
+ *
+ * Logical sign layout: word w of row m of base k holds columns 32w..32w+31,
+ * bit j of the word is column 32w+j.  A set bit is +1, a clear bit is -1.
+ *
+ * Device sign layout (what every kernel reads), for K bases of an M x N
+ * matrix with ND = N/32 words per row:
+ *   plane  = round_up(M*ND, 64)                     words per base
+ *   rb = m / 64, r = m % 64, h = min(64, M - 64*rb) rows in row block rb
+ *   g  = w / 4,  j = w % 4,  wg = min(4, ND - 4*g)  words in word group g
+ *   offset(k, m, w) = k*plane + rb*64*ND + g*4*h + r*wg + j
+ * i.e. tiles of 64 rows x 4 words (128 columns), each stored row-major, one
+ * after the other along the words of a 64-row block; the last row block and
+ * the last word group may be narrower.  A full tile is one contiguous KiB,
+ * which a 64-lane wavefront reads with one 16-byte load per lane.
+ */
+#ifndef BSG_H
+#define BSG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSG_API __attribute__((visibility("default")))
+
+typedef int32_t bsg_status;
+
+#define BSG_OK 0
+#define BSG_ERR_NULL (-1)        /* a required pointer is NULL */
+#define BSG_ERR_SHAPE (-2)       /* a size is negative, N % 32 != 0, a count out of range */
+#define BSG_ERR_DTYPE (-3)       /* unknown dtype code */
+#define BSG_ERR_ALIGN (-4)       /* a device pointer is not 16-byte aligned */
+#define BSG_ERR_UNSUPPORTED (-5) /* a valid combination this build does not implement */
+#define BSG_ERR_WORKSPACE (-6)   /* workspace missing or smaller than required */
+#define BSG_ERR_HIP (-7)         /* a HIP runtime call or kernel launch failed */
+
+/* Activation / input dtypes. */
+#define BSG_F32 0
+#define BSG_F16 1
+#define BSG_BF16 2
+
+/* bsq_pack flags. */
+#define BSG_PACK_COLSCALE 1
+
+/* Version of this ABI (bumped on any incompatible change). */
+BSG_API int32_t bsg_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+BSG_API const char* bsg_status_string(bsg_status status);
+
+/* Number of uint32 words of a device sign buffer for K bases of an M x N
+ * matrix (K * plane, see the layout above).  0 if a size is invalid. */
+BSG_API size_t bsg_layout_words(int K, int M, int N);
+
+/* Word offset of logical word w of row m of base k in the device layout, or
+ * -1 if an index is out of range.  A pure host function. */
+BSG_API int64_t bsg_layout_word_offset(int K, int M, int N, int k, int m, int w);
+
+/* Device workspace bytes needed by bs_gemv / bs_gemv_i8 for these sizes
+ * (0 when the launch plan needs none).  Every workspace starts with a
+ * 64 KiB area of arrival counters (one per 64-row block) followed by the
+ * per-split partial sums.  The counter area must be zero-filled before the
+ * workspace is first used; every completed call leaves it zero again, so
+ * one workspace serves calls of any size in sequence.  Calls that overlap
+ * in time must not share a workspace. */
+BSG_API size_t bsg_gemv_workspace_bytes(int K, int M, int N, int B);
+
+/* Device workspace bytes needed by binlr_apply (the counter area, z, and
+ * the partial sums of its two sign products); same zero-fill rule. */
+BSG_API size_t bsg_binlr_workspace_bytes(int r, int M, int N, int B);
+
+/* ------------------------------------------------------------------ */
+/* Packing (offline).                                                  */
+/* ------------------------------------------------------------------ */
+
+/* Device workspace bytes bsq_pack needs: the fp64 residual, 8*M*N bytes. */
+BSG_API size_t bsq_pack_workspace_bytes(int M, int N);
+
+/*
+ * bsq_pack -- greedy residual binary bases (FluxBin Sec. 2 and Sec. 3.1).
+ * For k = 1..K, on the residual R (R = W at first, kept in fp64):
+ *   B_k      = sign(R), sign(0) = +1                  -> bits (device layout)
+ *   alpha_k  = fp32( sum_n |R[m,n]| / N )   per row   -> alpha [K][M] fp32
+ *   c_k[n]   = fp16(fp32( sum_m alpha_k[m] |R[m,n]| / sum_m alpha_k[m]^2 ))
+ *              (least-squares column scale, 1 if the denominator is 0) when
+ *              flags has BSG_PACK_COLSCALE, else 1   -> colscale [K][N] fp16
+ *   R       <- R - alpha_k[m] c_k[n] B_k[m,n]         (stored, rounded scales)
+ * Every sum runs in fp64 in ascending index order, so the result is bit-exact
+ * with a sequential CPU implementation.
+ *   W         (device) fp32 [M][N], row-major; must hold no NaN (not checked)
+ *   bits      (device) uint32 [bsg_layout_words(K, M, N)]
+ *   alpha     (device) fp32 [K][M]
+ *   colscale  (device) uint16 (fp16 bits) [K][N]; required iff COLSCALE
+ *   workspace (device) >= bsq_pack_workspace_bytes(M, N)
+ * 1 <= K <= 8.
+ */
+BSG_API bsg_status bsq_pack(const float* W, int M, int N, int K, int flags,
+                    uint32_t* bits, float* alpha, uint16_t* colscale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bsq_pack_signs -- pack a real matrix S (device, fp32 [M][N]) into device
+ * sign layout with K = 1: bit = [S >= 0].  Used for the +-1 low-rank
+ * factors: U as an M x r matrix, V as an r x N matrix (BiLoCo "The core
+ * idea").  N % 32 == 0.
+ */
+BSG_API bsg_status bsq_pack_signs(const float* S, int M, int N, uint32_t* bits, void* stream);
+
+/*
+ * bsq_absmean -- activation statistic for choosing protected rows (BiSCo,
+ * "Sensitivity Protection"): xbar[n] = fp32( sum_s |X[s][n]| / S ) in fp64,
+ * s ascending.  X (device) fp32 [S][N]; xbar (device) fp32 [N].  Any N > 0.
+ */
+BSG_API bsg_status bsq_absmean(const float* X, int S, int N, float* xbar, void* stream);
+
+/* Device workspace bytes bsq_salient needs. */
+BSG_API size_t bsq_salient_workspace_bytes(int M, int N);
+
+/*
+ * bsq_salient -- protected int8 rows (BiSCo, "Sensitivity Protection"):
+ *   score_m = sum_n |W[m,n]| xbar[n]          (fp64, n ascending)
+ *   rows    = the ns highest scores, ties to the smaller m, ascending
+ *   s_i     = fp16(fp32( max_n |W[m,n]| / 127 ))         symmetric per row
+ *   q[i,n]  = clamp(rint_even(W[m,n] / s_i), -127, 127), 0 if s_i == 0
+ *   alpha[k][m] = 0 for every base k on the kept rows (the int8 row replaces
+ *   the binary row; the sign bits stay).
+ *   W (device) fp32 [M][N]; xbar (device) fp32 [N]; rows (device) int32 [ns];
+ *   q (device) int8 [ns][N]; s_f16 (device) uint16 [ns];
+ *   alpha (device) fp32 [K][M] (updated in place; may be NULL when K == 0).
+ * 0 <= ns <= M.  Any N > 0.
+ */
+BSG_API bsg_status bsq_salient(const float* W, int M, int N, const float* xbar, int ns,
+                       int32_t* rows, int8_t* q, uint16_t* s_f16,
+                       float* alpha, int K, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * bsq_quantize_i8 -- symmetric per-column int8 quantisation of activations
+ * for the int8 mode: sx[b] = fp32(max_n |x[n,b]| / 127) (fp32 division),
+ * xq = clamp(rint_even(fp32(x / sx)), -127, 127), 0 if sx == 0.
+ *   x (device) [N][B] of dtype x_dtype; xq (device) int8 [N][B];
+ *   sx (device) fp32 [B].  Any N > 0, B >= 1.
+ */
+BSG_API bsg_status bsq_quantize_i8(const void* x, int x_dtype, int N, int B,
+                           int8_t* xq, float* sx, void* stream);
+
+/* Device-side layout conversions (K bases, M x N, N % 32 == 0).
+ * logical (device) uint32 [K][M][N/32]; bits (device) device layout. */
+BSG_API bsg_status bsg_logical_to_layout(const uint32_t* logical, int K, int M, int N,
+                                 uint32_t* bits, void* stream);
+BSG_API bsg_status bsg_layout_to_logical(const uint32_t* bits, int K, int M, int N,
+                                 uint32_t* logical, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* The decode-time product (hot path).                                 */
+/* ------------------------------------------------------------------ */
+
+/*
+ * bs_gemv -- binary-base product (FluxBin Sec. 3.1 and Sec. 3.2):
+ *   y[m,b] (= or +=) sum_k alpha[k][m] * sum_n (2 bit_k(m,n) - 1) * c_k[n] * x[n,b]
+ *   bits      (device) device sign layout, K bases of M x N
+ *   alpha     (device) fp32 [K][M]
+ *   colscale  (device) fp16 bits [K][N], or NULL for c == 1
+ *   x         (device) [N][B] (element (n, b) at n*B + b) of dtype x_dtype
+ *   y         (device) fp32 [M][B]; overwritten when accumulate == 0,
+ *             added to otherwise
+ *   workspace (device) >= bsg_gemv_workspace_bytes(K, M, N, B) (may be NULL
+ *             when that is 0); zero-filled before first use
+ * 1 <= K <= 8, 1 <= B <= 64.  Accumulation is fp32; the result is within
+ * 2e-3 * sum_k |alpha_k[m]| * sum_n |c_k[n] x[n,b]| of the exact value.
+ */
+BSG_API bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const float* alpha,
+                   const uint16_t* colscale, const void* x, int x_dtype, int B,
+                   float* y, int accumulate, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * bs_gemv_i8 -- the same product with int8 activations, exact in integers:
+ *   acc[k][m][b] = sum_n (2 bit_k(m,n) - 1) * xq[n,b]            (int32, exact)
+ *   y[m,b] (= or +=) sx[b] * sum_k alpha[k][m] * acc[k][m][b]    (fp32)
+ *   xq (device) int8 [N][B]; sx (device) fp32 [B] (may be NULL iff y is NULL);
+ *   acc (device) int32 [K][M][B] or NULL; y (device) fp32 [M][B] or NULL
+ *   (at least one of acc, y).  No column scales in this mode.
+ * 1 <= K <= 8, 1 <= B <= 64, N <= 2^24.
+ */
+BSG_API bsg_status bs_gemv_i8(const uint32_t* bits, int K, int M, int N, const float* alpha,
+                      const int8_t* xq, const float* sx, int B, int32_t* acc,
+                      float* y, int accumulate, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * binlr_apply -- binary low-rank correction (BiLoCo "The core idea"):
+ *   z[j,b]  = alpha_r[j] * sum_n sv(j,n) * x[n,b]      (fp32, in the workspace)
+ *   y[m,b] += sum_j su(m,j) * z[j,b]
+ *   U_bits  (device) device sign layout of the M x r sign matrix (row m holds
+ *           u_j[m] for j = 0..r-1), K = 1
+ *   V_bits  (device) device sign layout of the r x N sign matrix, K = 1
+ *   alpha_r (device) fp16 bits [r]
+ * r % 32 == 0 (pad unused ranks with alpha_r = 0).  y always accumulates.
+ *   workspace (device) >= bsg_binlr_workspace_bytes(r, M, N, B)
+ */
+BSG_API bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits,
+                       const uint16_t* alpha_r, int r, int M, int N,
+                       const void* x, int x_dtype, int B, float* y,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * salient_int8_apply -- protected int8 rows (BiSCo "Sensitivity Protection"):
+ *   y[rows[i], b] += s_i * sum_n q[i][n] * x[n,b]
+ *   rows (device) int32 [ns], distinct, each in [0, M) (others are skipped);
+ *   q (device) int8 [ns][N]; s_f16 (device) fp16 bits [ns].
+ * Any N > 0 (q rows need no padding); 0 <= ns.  y always accumulates.
+ */
+BSG_API bsg_status salient_int8_apply(const int32_t* rows, int ns, const int8_t* q,
+                              const uint16_t* s_f16, int M, int N,
+                              const void* x, int x_dtype, int B, float* y,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSG_H */

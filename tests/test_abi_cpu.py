@@ -1,0 +1,159 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/bsg.h declares, computes layout offsets by the documented formula,
+and rejects invalid arguments before any HIP call.
+
+Every call below either is a pure host function or fails validation: no
+call here enqueues GPU work.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_gemv_packed_amd as bsg
+import oracle
+from bit_gemv_packed_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsg.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+
+# Fake device addresses: only ever passed to calls that fail validation.  As
+# a second guard, the tests that pass them are skipped where a GPU is
+# visible, so a validation slip can never launch a kernel on them.
+A16 = 0x100000
+A16b = 0x200000
+A16c = 0x300000
+A16d = 0x400000
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+fake_ptrs = pytest.mark.skipif(_gpu_visible(), reason="fake device pointers are only passed where no GPU is visible")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return re.findall(r"^BSG_API\s+[\w\s\*]+?\b(\w+)\s*\(", txt, flags=re.M)
+
+
+def test_header_declares_the_calls_the_pages_name():
+    names = set(_declared())
+    for n in ("bsq_pack", "bs_gemv", "binlr_apply", "salient_int8_apply"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(bsg.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings():
+    assert bsg.lib().bsg_abi_version() == 1
+    for s in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EUNSUP, EWS, EHIP):
+        assert len(bsg.status_string(s)) >= 2
+    assert bsg.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("K,M,N", [(1, 64, 128), (2, 70, 160), (3, 130, 32), (1, 1, 96), (2, 200, 544), (4, 257, 4096)])
+def test_layout_formula_matches_oracle(K, M, N):
+    assert bsg.layout_words(K, M, N) == oracle.layout_words(K, M, N)
+    rng = np.random.default_rng(K * M + N)
+    nd = N // 32
+    for _ in range(300):
+        k, m, w = int(rng.integers(K)), int(rng.integers(M)), int(rng.integers(nd))
+        assert bsg.layout_word_offset(K, M, N, k, m, w) == oracle.layout_offset(K, M, N, k, m, w)
+    assert bsg.layout_word_offset(K, M, N, K, 0, 0) == -1
+    assert bsg.layout_word_offset(K, M, N, 0, M, 0) == -1
+    assert bsg.layout_word_offset(K, M, N, 0, 0, nd) == -1
+    assert bsg.layout_words(K, M, 33) == 0
+
+
+def test_workspace_sizes():
+    # the 4096x4096 two-base product splits its input dimension: needs a workspace
+    assert bsg.gemv_workspace_bytes(2, 4096, 4096, 1) >= 65536
+    assert bsg.gemv_workspace_bytes(0, 4096, 4096, 1) == 0
+    assert bsg.binlr_workspace_bytes(512, 5120, 5120, 1) >= 65536 + 512 * 4
+    assert bsg.binlr_workspace_bytes(500, 5120, 5120, 1) == 0
+    assert bsg.lib().bsq_pack_workspace_bytes(100, 64) >= 100 * 64 * 8
+
+
+def _gemv(bits=A16, K=2, M=128, N=256, alpha=A16b, cs=None, x=A16c, dt=2, B=1, y=A16d, acc=0, ws=None, wsb=0):
+    return bsg.lib().bs_gemv(bits, K, M, N, alpha, cs, x, dt, B, y, acc, ws, wsb, None)
+
+
+@fake_ptrs
+def test_bs_gemv_validation():
+    assert _gemv(dt=7) == EDTYPE
+    assert _gemv(N=33) == ESHAPE
+    assert _gemv(N=0) == ESHAPE
+    assert _gemv(K=0) == ESHAPE
+    assert _gemv(K=9) == ESHAPE
+    assert _gemv(B=0) == ESHAPE
+    assert _gemv(B=65) == ESHAPE
+    assert _gemv(M=-1) == ESHAPE
+    assert _gemv(M=0) == OK                      # empty output: a no-op
+    assert _gemv(bits=None) == ENULL
+    assert _gemv(alpha=None) == ENULL
+    assert _gemv(x=None) == ENULL
+    assert _gemv(y=None) == ENULL
+    assert _gemv(bits=A16 + 4) == EALIGN
+    assert _gemv(alpha=A16b + 2) == EALIGN
+    assert _gemv(x=A16c + 1, dt=2) == EALIGN
+    assert _gemv(cs=A16 + 1) == EALIGN
+    # needs a workspace at this size
+    assert _gemv(K=2, M=4096, N=4096) == EWS
+    need = bsg.gemv_workspace_bytes(2, 4096, 4096, 1)
+    assert _gemv(K=2, M=4096, N=4096, ws=0x500000, wsb=16) == EWS
+    assert _gemv(K=2, M=4096, N=4096, ws=0x500008, wsb=need) == EALIGN
+
+
+@fake_ptrs
+def test_bs_gemv_i8_validation():
+    L = bsg.lib()
+    f = lambda **kw: L.bs_gemv_i8(kw.get("bits", A16), kw.get("K", 2), kw.get("M", 128), kw.get("N", 256),
+                                  kw.get("alpha", A16b), kw.get("xq", A16c), kw.get("sx", A16d), kw.get("B", 1),
+                                  kw.get("acc", A16), kw.get("y", None), 0, None, 0, None)
+    assert f(N=48) == ESHAPE
+    assert f(N=(1 << 24) + 32) == ESHAPE
+    assert f(acc=None, y=None) == ENULL
+    assert f(xq=None) == ENULL
+    assert f(y=A16d, sx=None) == ENULL
+    assert f(M=0) == OK
+
+
+@fake_ptrs
+def test_binlr_and_salient_validation():
+    L = bsg.lib()
+    assert L.binlr_apply(A16, A16b, A16c, 500, 64, 64, A16d, 2, 1, A16, None, 0, None) == ESHAPE
+    assert L.binlr_apply(A16, A16b, A16c, 32, 64, 64, A16d, 2, 1, A16, None, 0, None) == EWS
+    assert L.binlr_apply(None, A16b, A16c, 32, 64, 64, A16d, 2, 1, A16, None, 0, None) == ENULL
+    assert L.binlr_apply(A16, A16b, A16c, 32, 64, 64, A16d, 9, 1, A16, None, 0, None) == EDTYPE
+    assert L.salient_int8_apply(A16, 3, A16b, A16c, 64, 64, A16d, 2, 1, None, None) == ENULL
+    assert L.salient_int8_apply(A16, -1, A16b, A16c, 64, 64, A16d, 2, 1, A16, None) == ESHAPE
+    assert L.salient_int8_apply(A16, 0, A16b, A16c, 64, 64, A16d, 2, 1, A16, None) == OK
+    assert L.salient_int8_apply(A16 + 2, 3, A16b, A16c, 64, 64, A16d, 2, 1, A16, None) == EALIGN
+
+
+@fake_ptrs
+def test_pack_validation():
+    L = bsg.lib()
+    assert L.bsq_pack(A16, 64, 64, 0, 0, A16b, A16c, None, A16d, 1 << 20, None) == ESHAPE
+    assert L.bsq_pack(A16, 64, 48, 1, 0, A16b, A16c, None, A16d, 1 << 20, None) == ESHAPE
+    assert L.bsq_pack(A16, 64, 64, 1, 4, A16b, A16c, None, A16d, 1 << 20, None) == ESHAPE
+    assert L.bsq_pack(A16, 64, 64, 1, 1, A16b, A16c, None, A16d, 1 << 20, None) == ENULL
+    assert L.bsq_pack(A16, 64, 64, 1, 0, A16b + 4, A16c, None, A16d, 1 << 20, None) == EALIGN
+    assert L.bsq_pack(A16, 64, 64, 1, 0, A16b, A16c, None, A16d, 100, None) == EWS
+    assert L.bsq_salient(A16, 64, 64, A16b, 65, A16c, A16d, A16, A16b, 1, A16c, 1 << 20, None) == ESHAPE
+    assert L.bsq_quantize_i8(A16, 5, 64, 1, A16b, A16c, None) == EDTYPE
+    assert L.bsg_logical_to_layout(A16, 1, 64, 40, A16b, None) == ESHAPE

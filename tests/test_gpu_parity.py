@@ -1,0 +1,247 @@
+"""GPU parity: every entry point of the C ABI (through the Python binding)
+against the CPU oracle on the same seeded inputs.
+
+Integer results (sign bits, layouts, int8 codes, int32 accumulators, row
+indices, fp16/fp32 scales written by the packer) must match bit for bit;
+floating-point outputs must lie within the per-output bound
+2e-3 * (sum_k |alpha_k| sum_n |c_k x| + sum_j |alpha_r| sum_n |x| + |s| sum_n |q x|).
+Sizes span several 64x4-word tiles and ragged row blocks / word groups.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_gemv_packed_amd import synth
+from gpu_util import DEV, check_close, f16_dev, say, to_dev, u16, u32, x_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import bit_gemv_packed_amd as bsg  # noqa: E402
+
+
+def _layout(logical, K, M, N):
+    return bsg.bsg_logical_to_layout(to_dev(logical.view(np.int32)), K, M, N)
+
+
+# ------------------------------------------------------------------ layout
+@pytest.mark.parametrize("K,M,N", [(1, 64, 128), (2, 70, 160), (3, 130, 32), (2, 200, 544), (2, 1, 32), (1, 4097, 4096)])
+def test_layout_conversion_bit_exact(K, M, N):
+    say("layout", K, M, N)
+    L = synth.random_bits(K + M + N, K, M, N)
+    phys = _layout(L, K, M, N)
+    torch.cuda.synchronize()
+    ref = oracle.to_layout(L, K, M, N)
+    got = u32(phys)
+    plane = oracle.layout_words(K, M, N) // K
+    for k in range(K):   # padding words at the end of each plane are unspecified
+        np.testing.assert_array_equal(got[k * plane:k * plane + M * (N // 32)], ref[k * plane:k * plane + M * (N // 32)])
+    back = bsg.bsg_layout_to_logical(phys, K, M, N)
+    np.testing.assert_array_equal(u32(back).reshape(K, M, N // 32), L)
+
+
+# ------------------------------------------------------------------ bs_gemv
+GEMV_CASES = [
+    # K, M, N, B, colscale, x dtype, x distribution
+    (1, 256, 256, 1, False, "f32", "normal"),
+    (2, 300, 544, 1, True, "bf16", "normal"),
+    (3, 70, 96, 2, False, "f16", "normal"),
+    (2, 1000, 4096, 1, True, "bf16", "normal"),
+    (2, 129, 1056, 3, True, "bf16", "student_t3"),
+    (1, 64, 32, 1, False, "f32", "normal"),
+    (1, 1, 32, 1, True, "bf16", "normal"),
+    (2, 4096, 4096, 4, False, "bf16", "normal"),
+    (2, 333, 2080, 16, True, "bf16", "normal"),
+    (1, 50, 128, 20, False, "f32", "normal"),
+    (8, 65, 256, 1, True, "f32", "normal"),
+    (4, 2000, 768, 8, False, "bf16", "normal"),
+    (2, 5, 14336, 1, False, "bf16", "normal"),
+]
+
+
+def _gemv_inputs(case):
+    K, M, N, B, cs, dt, dist = case
+    seed = K * 7919 + M * 31 + N + B
+    L = synth.random_bits(seed, K, M, N)
+    alpha, csb = synth.random_scales(seed, K, M, N, cs)
+    x = synth.random_x(seed, N, B, dt, dist)
+    return L, alpha, csb, x
+
+
+@pytest.mark.parametrize("case", GEMV_CASES, ids=lambda c: "K%d_M%d_N%d_B%d_cs%d_%s_%s" % c)
+def test_bs_gemv_matches_oracle(case):
+    K, M, N, B, cs, dt, dist = case
+    say("bs_gemv", case)
+    L, alpha, csb, x = _gemv_inputs(case)
+    bits = _layout(L, K, M, N)
+    ad = to_dev(alpha)
+    cd = f16_dev(csb) if cs else None
+    xd = x_dev(x, dt)
+    y = bsg.bs_gemv(bits, K, M, N, ad, xd, colscale=cd)
+    torch.cuda.synchronize()
+    ref = oracle.sign_gemv(L, K, M, N, alpha, x, csb)
+    tol = oracle.tolerance(x, alpha=alpha, colscale_f16=csb)
+    check_close(y.cpu().numpy(), ref, tol, "bs_gemv %s" % (case,))
+    # a second call gives the same bits (fixed-order reduction)
+    y2 = bsg.bs_gemv(bits, K, M, N, ad, xd, colscale=cd)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+def test_bs_gemv_accumulate_and_negation():
+    case = (2, 700, 2048, 2, True, "bf16", "normal")
+    K, M, N, B, cs, dt, _ = case
+    say("bs_gemv accumulate/negation", case)
+    L, alpha, csb, x = _gemv_inputs(case)
+    bits = _layout(L, K, M, N)
+    nbits = _layout(~L, K, M, N)
+    ad, cd, xd = to_dev(alpha), f16_dev(csb), x_dev(x, dt)
+    y = bsg.bs_gemv(bits, K, M, N, ad, xd, colscale=cd)
+    yn = bsg.bs_gemv(nbits, K, M, N, ad, xd, colscale=cd)
+    y0 = torch.randn((M, B), dtype=torch.float32, device=DEV, generator=torch.Generator(DEV).manual_seed(3))
+    ya = y0.clone()
+    bsg.bs_gemv(bits, K, M, N, ad, xd, colscale=cd, y=ya, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(yn, -y), "negating every sign must negate y exactly"
+    ref = oracle.sign_gemv(L, K, M, N, alpha, x, csb)
+    tol = oracle.tolerance(x, alpha=alpha, colscale_f16=csb) + 1e-6 * np.abs(y0.cpu().numpy())
+    check_close(ya.cpu().numpy(), y0.cpu().numpy().astype(np.float64) + ref, tol, "accumulate")
+
+
+def test_bs_gemv_one_hot_reads_every_column():
+    K, M, N = 1, 130, 256
+    say("bs_gemv one-hot", K, M, N)
+    L = synth.random_bits(77, K, M, N)
+    alpha = np.ones((K, M), np.float32)
+    bits = _layout(L, K, M, N)
+    X = np.eye(N, dtype=np.float32)[:, :64]          # 64 one-hot columns as a batch
+    y = bsg.bs_gemv(bits, K, M, N, to_dev(alpha), x_dev(X, "f32"))
+    torch.cuda.synchronize()
+    ref = oracle.sign_gemv(L, K, M, N, alpha, X.astype(np.float64))
+    np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+# ------------------------------------------------------------------ int8 mode
+I8_CASES = [(1, 256, 256, 1), (2, 300, 544, 1), (3, 70, 96, 2), (2, 4096, 4096, 1), (2, 333, 2080, 16),
+            (1, 5, 14336, 3), (2, 129, 1056, 20)]
+
+
+@pytest.mark.parametrize("case", I8_CASES, ids=lambda c: "K%d_M%d_N%d_B%d" % c)
+def test_bs_gemv_i8_exact(case):
+    K, M, N, B = case
+    say("bs_gemv_i8", case)
+    seed = 5000 + K * 101 + M + N + B
+    L = synth.random_bits(seed, K, M, N)
+    alpha, _ = synth.random_scales(seed, K, M, N, False)
+    x = synth.random_x(seed, N, B, "bf16", "student_t3")
+    xq, sx = oracle.quantize_i8(x)
+    bits = _layout(L, K, M, N)
+    acc, y = bsg.bs_gemv_i8(bits, K, M, N, to_dev(alpha), to_dev(xq), to_dev(sx))
+    torch.cuda.synchronize()
+    ref_acc = oracle.sign_gemv_i8(L, K, M, N, xq)
+    np.testing.assert_array_equal(acc.cpu().numpy().astype(np.int64), ref_acc)
+    xt = xq.astype(np.float64) * sx.astype(np.float64)[None, :]
+    ref = oracle.sign_gemv(L, K, M, N, alpha, xt)
+    check_close(y.cpu().numpy(), ref, oracle.tolerance(xt, alpha=alpha), "bs_gemv_i8 y")
+
+
+def test_quantize_i8_bit_exact():
+    for (N, B, dt, dist) in [(4096, 1, "bf16", "normal"), (5120, 16, "bf16", "student_t3"), (96, 3, "f32", "normal"),
+                             (256, 2, "f16", "normal")]:
+        say("quantize", N, B, dt, dist)
+        x = synth.random_x(N + B, N, B, dt, dist)
+        xq, sx = bsg.bsq_quantize_i8(x_dev(x, dt))
+        torch.cuda.synchronize()
+        rq, rs = oracle.quantize_i8(x)
+        np.testing.assert_array_equal(xq.cpu().numpy(), rq)
+        np.testing.assert_array_equal(sx.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+# ------------------------------------------------------------------ low rank
+LR_CASES = [(32, 256, 256, 1, "f32"), (512, 5120, 5120, 1, "bf16"), (64, 100, 96, 3, "f16"),
+            (512, 1000, 2048, 16, "bf16"), (32, 1, 32, 1, "f32")]
+
+
+@pytest.mark.parametrize("case", LR_CASES, ids=lambda c: "r%d_M%d_N%d_B%d_%s" % c)
+def test_binlr_apply_matches_oracle(case):
+    r, M, N, B, dt = case
+    say("binlr", case)
+    g = np.random.default_rng(r + M + N + B)
+    u = np.where(g.integers(0, 2, (M, r)) == 1, 1.0, -1.0).astype(np.float32)
+    v = np.where(g.integers(0, 2, (r, N)) == 1, 1.0, -1.0).astype(np.float32)
+    ar = np.abs(g.normal(0, 0.005, r)).astype(np.float16).view(np.uint16)
+    x = synth.random_x(r + N, N, B, dt)
+    Ub, Vb = bsg.bsq_pack_signs(to_dev(u)), bsg.bsq_pack_signs(to_dev(v))
+    y0 = torch.zeros((M, B), dtype=torch.float32, device=DEV) + 0.5
+    bsg.binlr_apply(Ub, Vb, f16_dev(ar), r, M, N, x_dev(x, dt), y0)
+    torch.cuda.synchronize()
+    ub, vb = oracle.pack_signs(u), oracle.pack_signs(v)
+    np.testing.assert_array_equal(u32(bsg.bsg_layout_to_logical(Ub, 1, M, r)).reshape(M, -1), ub)
+    np.testing.assert_array_equal(u32(bsg.bsg_layout_to_logical(Vb, 1, r, N)).reshape(r, -1), vb)
+    ref = 0.5 + oracle.binlr(ub, vb, ar, r, M, N, x)
+    tol = oracle.tolerance(x, alpha_r_f16=ar, M=M) + 1e-6
+    check_close(y0.cpu().numpy(), ref, tol, "binlr %s" % (case,))
+
+
+# ------------------------------------------------------------------ protected rows
+SAL_CASES = [(256, 256, 3, 1), (13824, 5120, 138, 1), (100, 100, 5, 2), (5120, 13824, 51, 16), (64, 32, 64, 1)]
+
+
+@pytest.mark.parametrize("case", SAL_CASES, ids=lambda c: "M%d_N%d_ns%d_B%d" % c)
+def test_salient_apply_matches_oracle(case):
+    M, N, ns, B = case
+    say("salient_apply", case)
+    g = np.random.default_rng(M + N + ns)
+    rows = np.sort(g.choice(M, ns, replace=False)).astype(np.int32)
+    q = g.integers(-127, 128, (ns, N)).astype(np.int8)
+    s = g.uniform(1e-4, 1e-3, ns).astype(np.float16).view(np.uint16)
+    x = synth.random_x(M + N, N, B, "bf16", "student_t3")
+    y = torch.zeros((M, B), dtype=torch.float32, device=DEV)
+    bsg.salient_int8_apply(to_dev(rows), to_dev(q), f16_dev(s), M, N, x_dev(x, "bf16"), y)
+    torch.cuda.synchronize()
+    ref = oracle.salient(rows, q, s, M, N, x)
+    tol = oracle.tolerance(x, rows=rows, q=q, s_f16=s, M=M)
+    check_close(y.cpu().numpy(), ref, tol, "salient %s" % (case,))
+    # rows that are not protected stay exactly zero
+    other = np.setdiff1d(np.arange(M), rows)
+    assert not y.cpu().numpy()[other].any()
+
+
+# ------------------------------------------------------------------ packing
+PACK_CASES = [(256, 256, 1, False), (320, 544, 3, False), (130, 96, 2, True), (4096, 4096, 2, True),
+              (1, 32, 2, True), (70, 4096, 4, True)]
+
+
+@pytest.mark.parametrize("case", PACK_CASES, ids=lambda c: "M%d_N%d_K%d_cs%d" % c)
+def test_pack_bit_exact(case):
+    M, N, K, cs = case
+    say("bsq_pack", case)
+    W = synth.weights(M + N, K, M, N)
+    bits, alpha, csd = bsg.bsq_pack(to_dev(W), K, colscale=cs)
+    torch.cuda.synchronize()
+    rb, ra, rc = oracle.pack(W, K, cs)
+    np.testing.assert_array_equal(u32(bsg.bsg_layout_to_logical(bits, K, M, N)).reshape(K, M, -1), rb)
+    np.testing.assert_array_equal(alpha.cpu().numpy().view(np.uint32), ra.view(np.uint32))
+    if cs:
+        np.testing.assert_array_equal(u16(csd), rc)
+
+
+def test_absmean_and_salient_select_bit_exact():
+    for (M, N, ns, K) in [(256, 256, 3, 1), (13824, 5120, 138, 2), (1000, 96, 10, 2), (300, 64, 0, 1)]:
+        say("bsq_salient", M, N, ns, K)
+        w = synth.WORKLOADS[5]
+        W = synth.weights(5, 9, M, N)
+        W[7] = W[3]                    # tied scores
+        X = synth.calibration(w, 9, N, 128)
+        alpha = np.full((K, M), 0.5, np.float32)
+        xbar = bsg.bsq_absmean(to_dev(X))
+        ad = to_dev(alpha)
+        rows, q, s = bsg.bsq_salient(to_dev(W), xbar, ns, ad)
+        torch.cuda.synchronize()
+        rx = oracle.absmean(X)
+        np.testing.assert_array_equal(xbar.cpu().numpy().view(np.uint32), rx.view(np.uint32))
+        rr, rq, rs, ra = oracle.salient_select(W, rx, ns, alpha)
+        np.testing.assert_array_equal(rows.cpu().numpy(), rr)
+        np.testing.assert_array_equal(q.cpu().numpy(), rq)
+        np.testing.assert_array_equal(u16(s), rs)
+        np.testing.assert_array_equal(ad.cpu().numpy(), ra)
