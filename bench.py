@@ -93,13 +93,12 @@ def main():
     cs_r = cs.unsqueeze(0).repeat(ncopy, 1, 1).contiguous() if cs is not None else None
     xs = torch.from_numpy(np.ascontiguousarray(synth.activations(w, 0, N, ncopy).T)).to(torch.bfloat16).to(dev)
     ys = torch.empty((ncopy, M), dtype=torch.float32, device=dev)
-    ws = bsg.zeros_workspace(bsg.gemv_workspace_bytes(K, M, N, B), dev)
     torch.cuda.synchronize()
 
     def step(i):
         c = i % ncopy
         bsg.bs_gemv(bits_r[c], K, M, N, alpha_r[c], xs[c], colscale=cs_r[c] if cs_r is not None else None,
-                    y=ys[c], workspace=ws)
+                    y=ys[c])
 
     for i in range(args.warmup):
         step(i)

@@ -40,7 +40,6 @@ _SIGS = {
     "bsg_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "bsg_layout_words": (_SZ, [_I, _I, _I]),
     "bsg_layout_word_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
-    "bsg_gemv_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "bsg_binlr_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "bsq_pack_workspace_bytes": (_SZ, [_I, _I]),
     "bsq_salient_workspace_bytes": (_SZ, [_I, _I]),
@@ -51,8 +50,8 @@ _SIGS = {
     "bsq_quantize_i8": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P]),
     "bsg_logical_to_layout": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P]),
     "bsg_layout_to_logical": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P]),
-    "bs_gemv": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, _SZ, _P]),
-    "bs_gemv_i8": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _I, _P, _SZ, _P]),
+    "bs_gemv": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P]),
+    "bs_gemv_i8": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _I, _P]),
     "binlr_apply": (ctypes.c_int32, [_P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P, _SZ, _P]),
     "salient_int8_apply": (ctypes.c_int32, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _P]),
 }
@@ -125,17 +124,17 @@ def _xshape(x, N: int) -> int:
     return x.shape[1]
 
 
-def zeros_workspace(nbytes: int, device) -> Optional["object"]:
-    """A zero-filled device workspace of nbytes (None when nbytes == 0)."""
+def new_workspace(nbytes: int, device) -> Optional["object"]:
+    """A device workspace of at least nbytes, 16-byte aligned (None when nbytes == 0)."""
     if nbytes == 0:
         return None
     torch = _torch()
-    return torch.zeros((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
+    return torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
 
 
 class Workspace:
-    """Per-device cache of zero-filled workspaces, reused across calls on one
-    stream (every completed call leaves its workspace zero-filled)."""
+    """Per-device cache of one workspace, grown on demand.  Calls through the
+    binding are stream-ordered on the current stream, so they may share it."""
 
     def __init__(self):
         self._bufs = {}
@@ -143,10 +142,10 @@ class Workspace:
     def get(self, nbytes: int, device):
         if nbytes == 0:
             return None
-        key = (str(device), "ws")
+        key = str(device)
         buf = self._bufs.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = zeros_workspace(max(nbytes, 1 << 20), device)
+            buf = new_workspace(max(nbytes, 1 << 20), device)
             self._bufs[key] = buf
         return buf
 
@@ -167,10 +166,6 @@ def layout_words(K: int, M: int, N: int) -> int:
 
 def layout_word_offset(K: int, M: int, N: int, k: int, m: int, w: int) -> int:
     return int(lib().bsg_layout_word_offset(K, M, N, k, m, w))
-
-
-def gemv_workspace_bytes(K: int, M: int, N: int, B: int) -> int:
-    return int(lib().bsg_gemv_workspace_bytes(K, M, N, B))
 
 
 def binlr_workspace_bytes(r: int, M: int, N: int, B: int) -> int:
@@ -256,24 +251,20 @@ def bsg_layout_to_logical(bits, K: int, M: int, N: int):
 
 
 # ------------------------------------------------------------------ hot path
-def bs_gemv(bits, K: int, M: int, N: int, alpha, x, colscale=None, y=None, accumulate: bool = False,
-            workspace=None):
+def bs_gemv(bits, K: int, M: int, N: int, alpha, x, colscale=None, y=None, accumulate: bool = False):
     """y (fp32 [M][B]) = or += sum_k alpha_k (.) (B_k (c_k (.) x)).  x: [N] or [N][B]."""
     torch = _torch()
     B = _xshape(x, N)
     dev = x.device
     if y is None:
         y = torch.empty((M, B), dtype=torch.float32, device=dev)
-    nb = gemv_workspace_bytes(K, M, N, B)
-    ws = workspace if workspace is not None else _WS.get(nb, dev)
-    wp, wn = _ws_args(ws)
     _check("bs_gemv", lib().bs_gemv(_ptr(bits), K, M, N, _ptr(alpha), _ptr(colscale), _ptr(x), _dtype_code(x), B,
-                                    _ptr(y), 1 if accumulate else 0, wp, wn, _stream(dev)))
+                                    _ptr(y), 1 if accumulate else 0, _stream(dev)))
     return y
 
 
 def bs_gemv_i8(bits, K: int, M: int, N: int, alpha, xq, sx, want_acc: bool = True, want_y: bool = True,
-               y=None, accumulate: bool = False, workspace=None) -> Tuple[Optional[object], Optional[object]]:
+               y=None, accumulate: bool = False) -> Tuple[Optional[object], Optional[object]]:
     """Exact int8-activation product.  Returns (acc int32 [K][M][B] or None, y fp32 [M][B] or None)."""
     torch = _torch()
     B = _xshape(xq, N)
@@ -283,11 +274,8 @@ def bs_gemv_i8(bits, K: int, M: int, N: int, alpha, xq, sx, want_acc: bool = Tru
         y = torch.empty((M, B), dtype=torch.float32, device=dev)
     if not want_y:
         y = None
-    nb = gemv_workspace_bytes(K, M, N, B)
-    ws = workspace if workspace is not None else _WS.get(nb, dev)
-    wp, wn = _ws_args(ws)
     _check("bs_gemv_i8", lib().bs_gemv_i8(_ptr(bits), K, M, N, _ptr(alpha), _ptr(xq), _ptr(sx), B, _ptr(acc),
-                                          _ptr(y), 1 if accumulate else 0, wp, wn, _stream(dev)))
+                                          _ptr(y), 1 if accumulate else 0, _stream(dev)))
     return acc, y
 
 

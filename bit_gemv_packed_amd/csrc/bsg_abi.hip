@@ -35,12 +35,11 @@ bool bad_n(int N) { return N <= 0 || (N % 32) != 0; }
 
 bsg_status hip_status(hipError_t e) { return e == hipSuccess ? BSG_OK : BSG_ERR_HIP; }
 
-// binlr workspace: [counters][z fp32 [r][B]][partials of whichever pass needs more]
-size_t binlr_ws(int r, int M, int N, int B) {
-  const GemvPlan pv = plan_gemv(1, r, N, B, false);
-  const GemvPlan pu = plan_gemv(1, M, r, B, false);
-  const size_t part = pv.part_bytes > pu.part_bytes ? pv.part_bytes : pu.part_bytes;
-  return kCounterBytes + align_up((size_t)r * B * 4, 256) + part;
+// binlr workspace: z, fp32 [r][B]
+size_t binlr_ws(int r, int B) { return align_up((size_t)r * B * 4, 256); }
+
+bool xvec_ok(const void* x, const void* cs) {
+  return (((uintptr_t)x) % 16) == 0 && (((uintptr_t)cs) % 8) == 0;
 }
 
 }  // namespace
@@ -74,16 +73,9 @@ int64_t bsg_layout_word_offset(int K, int M, int N, int k, int m, int w) {
   return (int64_t)layout_offset(M, N / 32, plane_words(M, N / 32), k, m, w);
 }
 
-size_t bsg_gemv_workspace_bytes(int K, int M, int N, int B) {
-  if (K < 1 || K > kMaxK || M <= 0 || bad_n(N) || B < 1 || B > kMaxB) return 0;
-  const GemvPlan pf = plan_gemv(K, M, N, B, false);
-  const GemvPlan pi = plan_gemv(K, M, N, B, true);
-  return pf.ws_bytes > pi.ws_bytes ? pf.ws_bytes : pi.ws_bytes;
-}
-
 size_t bsg_binlr_workspace_bytes(int r, int M, int N, int B) {
   if (r <= 0 || (r % 32) != 0 || M < 0 || bad_n(N) || B < 1 || B > kMaxB) return 0;
-  return binlr_ws(r, M > 0 ? M : 1, N, B);
+  return binlr_ws(r, B);
 }
 
 size_t bsq_pack_workspace_bytes(int M, int N) {
@@ -163,25 +155,21 @@ bsg_status bsg_layout_to_logical(const uint32_t* bits, int K, int M, int N, uint
 }
 
 bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const float* alpha, const uint16_t* colscale,
-                   const void* x, int x_dtype, int B, float* y, int accumulate, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   const void* x, int x_dtype, int B, float* y, int accumulate, void* stream) {
   if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
   if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || B < 1 || B > kMaxB) return BSG_ERR_SHAPE;
   if (M == 0) return BSG_OK;
   if (!bits || !alpha || !x || !y) return BSG_ERR_NULL;
   if (misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(colscale, 2) ||
-      misaligned(x, dtype_size(x_dtype)) || misaligned(y, 4) || misaligned(workspace, 16))
+      misaligned(x, dtype_size(x_dtype)) || misaligned(y, 4))
     return BSG_ERR_ALIGN;
-  const GemvPlan p = plan_gemv(K, M, N, B, false);
-  if (p.ws_bytes && (!workspace || workspace_bytes < p.ws_bytes)) return BSG_ERR_WORKSPACE;
-  GemvArgs a{};
+  const ProdPlan p = plan_prod(K, M, N, B, colscale != nullptr, false);
+  ProdArgs a{};
   a.bits = bits;
   a.alpha = alpha;
   a.colscale = colscale;
   a.x = x;
   a.y = y;
-  a.cnt = p.ws_bytes ? (unsigned*)workspace : nullptr;
-  a.part = p.ws_bytes ? (float*)((char*)workspace + kCounterBytes) : nullptr;
   a.plane = plane_words(M, N / 32);
   a.K = K;
   a.M = M;
@@ -190,31 +178,25 @@ bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const float* alpha
   a.B = B;
   a.xdt = x_dtype;
   a.accumulate = accumulate ? 1 : 0;
-  a.S = p.S;
-  a.wb = p.wb;
-  return hip_status(launch_gemv_f(a, p, (hipStream_t)stream));
+  a.xvec = xvec_ok(x, colscale);
+  return hip_status(launch_prod_f(a, p, (hipStream_t)stream));
 }
 
 bsg_status bs_gemv_i8(const uint32_t* bits, int K, int M, int N, const float* alpha, const int8_t* xq,
-                      const float* sx, int B, int32_t* acc, float* y, int accumulate, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      const float* sx, int B, int32_t* acc, float* y, int accumulate, void* stream) {
   if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || N > (1 << 24) || B < 1 || B > kMaxB) return BSG_ERR_SHAPE;
   if (M == 0) return BSG_OK;
   if (!bits || !xq || (!acc && !y) || (y && (!alpha || !sx))) return BSG_ERR_NULL;
-  if (misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(sx, 4) || misaligned(acc, 4) ||
-      misaligned(y, 4) || misaligned(workspace, 16))
+  if (misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(sx, 4) || misaligned(acc, 4) || misaligned(y, 4))
     return BSG_ERR_ALIGN;
-  const GemvPlan p = plan_gemv(K, M, N, B, true);
-  if (p.ws_bytes && (!workspace || workspace_bytes < p.ws_bytes)) return BSG_ERR_WORKSPACE;
-  GemvI8Args a{};
+  const ProdPlan p = plan_prod(K, M, N, B, false, true);
+  ProdArgs a{};
   a.bits = bits;
   a.alpha = alpha;
   a.xq = xq;
   a.sx = sx;
   a.acc = acc;
   a.y = y;
-  a.cnt = p.ws_bytes ? (unsigned*)workspace : nullptr;
-  a.part = p.ws_bytes ? (int32_t*)((char*)workspace + kCounterBytes) : nullptr;
   a.plane = plane_words(M, N / 32);
   a.K = K;
   a.M = M;
@@ -222,9 +204,7 @@ bsg_status bs_gemv_i8(const uint32_t* bits, int K, int M, int N, const float* al
   a.ND = N / 32;
   a.B = B;
   a.accumulate = accumulate ? 1 : 0;
-  a.S = p.S;
-  a.wb = p.wb;
-  return hip_status(launch_gemv_i8(a, p, (hipStream_t)stream));
+  return hip_status(launch_prod_i8(a, p, (hipStream_t)stream));
 }
 
 bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uint16_t* alpha_r, int r, int M,
@@ -237,22 +217,16 @@ bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uin
   if (misaligned(U_bits, 16) || misaligned(V_bits, 16) || misaligned(alpha_r, 2) ||
       misaligned(x, dtype_size(x_dtype)) || misaligned(y, 4) || misaligned(workspace, 16))
     return BSG_ERR_ALIGN;
-  if (!workspace || workspace_bytes < binlr_ws(r, M, N, B)) return BSG_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < binlr_ws(r, B)) return BSG_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  const GemvPlan pv = plan_gemv(1, r, N, B, false);
-  const GemvPlan pu = plan_gemv(1, M, r, B, false);
-  char* ws = (char*)workspace;
-  unsigned* cnt = (unsigned*)ws;
-  float* z = (float*)(ws + kCounterBytes);
-  float* part = (float*)(ws + kCounterBytes + align_up((size_t)r * B * 4, 256));
+  float* z = (float*)workspace;
 
-  GemvArgs v{};
+  // z = alpha_r (.) (V x): a one-base sign product with fp16 row scales
+  ProdArgs v{};
   v.bits = V_bits;
   v.alpha_h = alpha_r;
   v.x = x;
   v.y = z;
-  v.part = part;
-  v.cnt = cnt;
   v.plane = plane_words(r, N / 32);
   v.K = 1;
   v.M = r;
@@ -261,17 +235,15 @@ bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uin
   v.B = B;
   v.xdt = x_dtype;
   v.accumulate = 0;
-  v.S = pv.S;
-  v.wb = pv.wb;
-  hipError_t e = launch_gemv_f(v, pv, st);
+  v.xvec = xvec_ok(x, nullptr);
+  hipError_t e = launch_prod_f(v, plan_prod(1, r, N, B, false, false), st);
   if (e != hipSuccess) return BSG_ERR_HIP;
 
-  GemvArgs u{};
+  // y += U z: a one-base sign product over the r ranks with unit row scales
+  ProdArgs u{};
   u.bits = U_bits;
   u.x = z;
   u.y = y;
-  u.part = part;
-  u.cnt = cnt;
   u.plane = plane_words(M, r / 32);
   u.K = 1;
   u.M = M;
@@ -280,9 +252,8 @@ bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uin
   u.B = B;
   u.xdt = BSG_F32;
   u.accumulate = 1;
-  u.S = pu.S;
-  u.wb = pu.wb;
-  return hip_status(launch_gemv_f(u, pu, st));
+  u.xvec = 1;
+  return hip_status(launch_prod_f(u, plan_prod(1, M, r, B, false, false), st));
 }
 
 bsg_status salient_int8_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s_f16, int M, int N,

@@ -1,314 +1,200 @@
-// Sign-GEMV kernels for gfx950: the binary-base product with fp32
-// accumulation through per-workgroup activation tables, and the exact int8
-// variant through activation bit planes and popcounts.
+// Binary-base product for gfx950 (float activations):
 //
-// Mapping (both kernels): one wavefront per 64-row block, lane = row.  Every
-// lane walks the same sign words of its own row, so all 64 lanes of a wave
-// index the same activation table at the same time: the table reads are
-// broadcasts that never conflict across LDS banks.  A 16-byte load per lane
-// of a 64x4-word layout tile is one contiguous KiB per wavefront.
+//   y[m,b] (= or +=) sum_k alpha_k[m] sum_n (2 bit_k(m,n) - 1) c_k[n] x[n,b]
 //
-// Activation tables (FluxBin Sec. 2 "LUT-based Multiplication" and Sec. 3.2
-// Stage 1, with the column scale folded into x first): for every group of 4
-// input columns the workgroup stores the 16 signed sums +-x0 +-x1 +-x2 +-x3;
-// a 4-bit slice of a sign word is the table index, so one LDS read and one
-// add replace four signed adds.  Tables hold fp32 values; accumulation is
-// fp32.
+// Work decomposition.  A workgroup owns RW = 64/Q complete output rows, so
+// no reduction crosses workgroups: the result is deterministic and needs no
+// workspace.  Q lanes of a wavefront share a row.  The W wavefronts of the
+// workgroup split the input dimension into chunks of CW = Q*NWL sign words
+// (NCH chunks each); inside a chunk, the lanes of quarter q read NWL
+// consecutive words of their row.  The Q partial sums of a row are combined
+// by two lane shuffles, the W wavefront sums through LDS, in a fixed order.
 //
-// int8 mode: sum_n s(n) xq(n) = 2 * sum_{bit=1} xq - sum xq, and
-// sum_{bit=1} xq = sum_p 2^p popcount(word & plane_p) - 128 popcount(word &
-// plane_7) over the two's-complement bit planes of xq: 8 AND + 8 popcount per
-// 32 weights, exact in int32.
-//
-// Splits: when a row block alone gives too few workgroups, the input
-// dimension is split across S workgroups.  Each writes fp32 (or int32)
-// partial sums to the workspace; the last workgroup to arrive at a row block
-// (an arrival counter per row block) adds the S partials in split order, so
-// the result does not depend on scheduling, and resets the counter.
-#include "bsg_internal.h"
+// Activation tables (FluxBin Sec. 2 "LUT-based Multiplication": split x into
+// sub-vectors, precompute every signed combination, use the weight bit
+// pattern as the table address; Sec. 3.2 Stage 1: fold the column scale into
+// x while building the table).  Sub-vectors are 4 columns wide: 16 fp32
+// entries per table.  Each wavefront builds the tables of its own chunk in
+// its own LDS region, laid out [step][quarter][16 entries], so at every
+// lookup the lanes of a quarter read one 64-byte table and the Q tables of
+// one instruction occupy disjoint bank groups: the reads never conflict.
+// Table addresses take one SDWA add per 4-bit slice: the sign word is
+// rotated by 2 bits each way and masked once, after which byte j of the
+// masked rotation is (slice value) * 4.  Per 32 weights: 2 rotates, 2 masks,
+// 8 SDWA adds, 8 LDS reads and 8 fp32 adds.
+#include "bsg_prod.h"
 
 #include <cstdlib>
 
 namespace bsg {
 
-__device__ inline void agent_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent"); }
+// A float at an LDS byte address (the address already includes the base of
+// the dynamic LDS block), read with the address in one VGPR.
+typedef __attribute__((address_space(3))) const float lds_cf32;
+__device__ inline float lds_f32(uint32_t addr) { return *(lds_cf32*)(uintptr_t)addr; }
 
-// Returns true in every lane of the workgroup that arrives last at row block rb.
-__device__ inline bool arrive_last(unsigned* cnt, int rb, int S) {
-  __shared__ int s_last;
-  agent_fence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned prev = __hip_atomic_fetch_add(cnt + rb, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (unsigned)(S - 1));
-  }
-  __syncthreads();
-  bool last = s_last != 0;
-  if (last) agent_fence();
-  return last;
-}
-
-__device__ inline void reset_counter(unsigned* cnt, int rb) {
-  if (threadIdx.x == 0) __hip_atomic_store(cnt + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ inline float row_alpha(const GemvArgs& a, int k, int m) {
+__device__ inline float row_alpha(const ProdArgs& a, int k, int m) {
   if (a.alpha) return a.alpha[(size_t)k * a.M + m];
   if (a.alpha_h) return f16_bits_to_float(a.alpha_h[(size_t)k * a.M + m]);
   return 1.0f;
 }
 
-// Loads the (up to) 4 words of row `lane` of one layout tile.
-__device__ inline void load_tile_words(const uint32_t* tile, int lane, int wg, uint32_t wd[4]) {
-  if (wg == 4) {
-    uint4 v = *(const uint4*)(tile + (size_t)lane * 4);
-    wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
-  } else {
-    for (int j = 0; j < 4; ++j) wd[j] = j < wg ? tile[(size_t)lane * wg + j] : 0u;
-  }
-}
+template <int Q, int NWL, int KM, int BB>
+__global__ void __launch_bounds__(1024) k_prod_f(ProdArgs a) {
+  constexpr int RW = 64 / Q;
+  constexpr int CW = Q * NWL;
+  constexpr int STEPS = NWL * 8;      // 4-column groups per lane per chunk
+  constexpr uint32_t REG = CW * 512;  // bytes of one (base, batch column) table set
+  extern __shared__ __align__(16) char lds[];
 
-template <int BB>
-__global__ void __launch_bounds__(64) k_gemv_f(GemvArgs a) {
-  extern __shared__ __align__(16) float lut[];  // [KX][BB][G][16]
-  const int lane = threadIdx.x;
-  const int s = blockIdx.x;
-  const int rb = blockIdx.y;
-  const int w0 = s * a.wb;
-  const int nw = min(a.wb, a.ND - w0);
-  const int G = nw * 8;
-  const int KX = a.colscale ? a.K : 1;
-
-  // Stage: x' = c (.) x, then the 16 signed sums of every 4-column group.
-  for (int idx = lane; idx < KX * BB * G; idx += 64) {
-    const int g = idx % G;
-    const int t = idx / G;
-    const int b = t % BB;
-    const int kx = t / BB;
-    const int n0 = w0 * 32 + g * 4;
-    const bool bok = (a.b0 + b) < a.B;
-    float xv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v = bok ? load_x(a.x, a.xdt, (size_t)(n0 + j) * a.B + a.b0 + b) : 0.0f;
-      if (a.colscale) v *= f16_bits_to_float(a.colscale[(size_t)kx * a.N + n0 + j]);
-      xv[j] = v;
-    }
-    const float p0 = xv[0] + xv[1], m0 = xv[0] - xv[1];
-    const float p1 = xv[2] + xv[3], m1 = xv[2] - xv[3];
-    const float A0 = -p0, A1 = m0, A2 = -m0, A3 = p0;
-    const float Q[4] = {-p1, m1, -m1, p1};
-    float4* dst = (float4*)(lut + ((size_t)(kx * BB + b) * G + g) * 16);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = make_float4(A0 + Q[q], A1 + Q[q], A2 + Q[q], A3 + Q[q]);
-  }
-  __syncthreads();
-
-  const int m = rb * 64 + lane;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int q = lane / RW;
+  const int r = lane % RW;
+  const int m = blockIdx.x * RW + r;
   const bool valid = m < a.M;
-  const int h = min(64, a.M - rb * 64);
+  const bool cs = a.colscale != nullptr;
+  const int KX = cs ? a.K : 1;
+  const uint32_t wbase_lds = (uint32_t)wv * a.wave_lds;
+
+  float acc[KM][BB];
+#pragma unroll
+  for (int k = 0; k < KM; ++k)
+#pragma unroll
+    for (int b = 0; b < BB; ++b) acc[k][b] = 0.0f;
+
+  // Sign words of the first chunk are requested before anything else, so
+  // their latency overlaps the table build.
+  uint32_t cur[KM][NWL], nxt[KM][NWL];
+  load_chunk<KM, NWL>(a, valid, m, wv * a.NCH * CW + q * NWL, cur);
+
+  for (int c = 0; c < a.NCH; ++c) {
+    const int cw0 = (wv * a.NCH + c) * CW;  // first word of the chunk
+    if (c + 1 < a.NCH) load_chunk<KM, NWL>(a, valid, m, cw0 + CW + q * NWL, nxt);
+
+    // ---- tables: the 16 signed sums of every 4-column group of the chunk
+    const int items = KX * BB * CW * 8;
+    for (int it = lane; it < items; it += 64) {
+      const int g = it % (CW * 8);
+      const int t = it / (CW * 8);
+      const int b = t % BB;
+      const int kx = t / BB;
+      const int n0 = cw0 * 32 + g * 4;
+      float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (n0 < a.N && a.b0 + b < a.B) {
+        if (a.B == 1 && a.xvec && a.xdt != BSG_F32) {
+          const uint2 v = *(const uint2*)((const uint16_t*)a.x + n0);
+          const uint16_t hv[4] = {(uint16_t)(v.x & 0xffffu), (uint16_t)(v.x >> 16), (uint16_t)(v.y & 0xffffu),
+                                  (uint16_t)(v.y >> 16)};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            xv[j] = a.xdt == BSG_BF16 ? bf16_bits_to_float(hv[j]) : f16_bits_to_float(hv[j]);
+        } else if (a.B == 1 && a.xvec) {
+          const float4 v = *(const float4*)((const float*)a.x + n0);
+          xv[0] = v.x;
+          xv[1] = v.y;
+          xv[2] = v.z;
+          xv[3] = v.w;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xv[j] = load_x(a.x, a.xdt, (size_t)(n0 + j) * a.B + a.b0 + b);
+        }
+        if (cs && a.xvec) {
+          const uint2 cv = *(const uint2*)(a.colscale + (size_t)kx * a.N + n0);
+          xv[0] *= f16_bits_to_float((uint16_t)(cv.x & 0xffffu));
+          xv[1] *= f16_bits_to_float((uint16_t)(cv.x >> 16));
+          xv[2] *= f16_bits_to_float((uint16_t)(cv.y & 0xffffu));
+          xv[3] *= f16_bits_to_float((uint16_t)(cv.y >> 16));
+        } else if (cs) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xv[j] *= f16_bits_to_float(a.colscale[(size_t)kx * a.N + n0 + j]);
+        }
+      }
+      // entry e = sum_j (2 bit_j(e) - 1) xv[j]: bits 0,1 pick the first pair sum, bits 2,3 the second
+      const float p0 = xv[0] + xv[1], m0 = xv[0] - xv[1];
+      const float p1 = xv[2] + xv[3], m1 = xv[2] - xv[3];
+      const float hi[4] = {-p1, m1, -m1, p1};
+      const int qq = g / STEPS, ii = g % STEPS;
+      float4* dst = (float4*)(lds + wbase_lds + (uint32_t)(kx * BB + b) * REG + (uint32_t)(ii * Q + qq) * 64);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = make_float4(-p0 + hi[e], m0 + hi[e], -m0 + hi[e], p0 + hi[e]);
+    }
+    __syncthreads();
+
+    // ---- lookups: one table read and one add per 4 weights
+    const int lw0 = cw0 + q * NWL;  // this lane's first word in the chunk
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k < a.K) {
+        const uint32_t lbase =
+            (uint32_t)(uintptr_t)(lds + wbase_lds + (uint32_t)(cs ? k : 0) * BB * REG + (uint32_t)q * 64);
+#pragma unroll
+        for (int j = 0; j < NWL; ++j) {
+          if (valid && lw0 + j < a.ND) {
+            const uint32_t word = cur[k][j];
+            const uint32_t rl = __builtin_amdgcn_alignbit(word, word, 30) & 0x3c3c3c3cu;  // even slices * 4
+            const uint32_t rr = __builtin_amdgcn_alignbit(word, word, 2) & 0x3c3c3c3cu;   // odd slices * 4
+            uint32_t ad[8];
+            ad[0] = byte_add<0>(lbase, rl);
+            ad[1] = byte_add<0>(lbase, rr);
+            ad[2] = byte_add<1>(lbase, rl);
+            ad[3] = byte_add<1>(lbase, rr);
+            ad[4] = byte_add<2>(lbase, rl);
+            ad[5] = byte_add<2>(lbase, rr);
+            ad[6] = byte_add<3>(lbase, rl);
+            ad[7] = byte_add<3>(lbase, rr);
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+#pragma unroll
+              for (int b = 0; b < BB; ++b)
+                acc[k][b] += lds_f32(ad[n] + (uint32_t)((j * 8 + n) * Q * 64) + (uint32_t)b * REG);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (c + 1 < a.NCH) {
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+#pragma unroll
+        for (int j = 0; j < NWL; ++j) cur[k][j] = nxt[k][j];
+    }
+  }
+
+  // ---- row scales, then the Q lanes of a row, then the W wavefronts
   float tot[BB];
 #pragma unroll
   for (int b = 0; b < BB; ++b) tot[b] = 0.0f;
-
-  if (valid) {
-    for (int k = 0; k < a.K; ++k) {
-      const float* L = lut + (size_t)(a.colscale ? k : 0) * BB * G * 16;
-      const uint32_t* base_k = a.bits + (size_t)k * a.plane + (size_t)rb * 64 * a.ND;
-      float acc[BB];
-#pragma unroll
-      for (int b = 0; b < BB; ++b) acc[b] = 0.0f;
-      for (int gw = 0; gw < nw; gw += 4) {
-        const int g4 = (w0 + gw) >> 2;
-        const int wg = min(4, a.ND - 4 * g4);
-        uint32_t wd[4];
-        load_tile_words(base_k + (size_t)g4 * 4 * h, lane, wg, wd);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j < wg) {
-            const uint32_t word = wd[j];
-            const float* Lw = L + (size_t)(gw + j) * 8 * 16;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int e = (word >> (4 * i)) & 15;
-#pragma unroll
-              for (int b = 0; b < BB; ++b) acc[b] += Lw[((size_t)b * G + i) * 16 + e];
-            }
-          }
-        }
-      }
-      const float al = row_alpha(a, k, m);
-#pragma unroll
-      for (int b = 0; b < BB; ++b) tot[b] += al * acc[b];
-    }
-  }
-
-  if (a.S == 1) {
-    if (valid) {
-#pragma unroll
-      for (int b = 0; b < BB; ++b) {
-        if (a.b0 + b < a.B) {
-          const size_t yi = (size_t)m * a.B + a.b0 + b;
-          a.y[yi] = (a.accumulate ? a.y[yi] : 0.0f) + tot[b];
-        }
-      }
-    }
-    return;
-  }
-
   if (valid) {
 #pragma unroll
-    for (int b = 0; b < BB; ++b) a.part[((size_t)s * a.M + m) * BB + b] = tot[b];
-  }
-  if (!arrive_last(a.cnt, rb, a.S)) return;
-  if (valid) {
-    float sum[BB];
+    for (int k = 0; k < KM; ++k) {
+      if (k < a.K) {
+        const float al = row_alpha(a, k, m);
 #pragma unroll
-    for (int b = 0; b < BB; ++b) sum[b] = 0.0f;
-    for (int s2 = 0; s2 < a.S; ++s2) {
-#pragma unroll
-      for (int b = 0; b < BB; ++b) sum[b] += a.part[((size_t)s2 * a.M + m) * BB + b];
-    }
-#pragma unroll
-    for (int b = 0; b < BB; ++b) {
-      if (a.b0 + b < a.B) {
-        const size_t yi = (size_t)m * a.B + a.b0 + b;
-        a.y[yi] = (a.accumulate ? a.y[yi] : 0.0f) + sum[b];
+        for (int b = 0; b < BB; ++b) tot[b] += al * acc[k][b];
       }
     }
   }
-  reset_counter(a.cnt, rb);
-}
-
-template <int BB>
-__global__ void __launch_bounds__(64) k_gemv_i8(GemvI8Args a) {
-  extern __shared__ __align__(16) uint32_t sh[];  // planes [nw][BB][8], then column sums [nw][BB]
-  const int lane = threadIdx.x;
-  const int s = blockIdx.x;
-  const int rb = blockIdx.y;
-  const int w0 = s * a.wb;
-  const int nw = min(a.wb, a.ND - w0);
-  uint32_t* planes = sh;
-  int* csum = (int*)(sh + (size_t)nw * BB * 8);
-
-  // Stage: two's-complement bit planes of xq for every sign word, and the
-  // column sums of xq per word.
-  for (int idx = lane; idx < nw * BB; idx += 64) {
-    const int w = idx / BB;
-    const int b = idx % BB;
-    const bool bok = (a.b0 + b) < a.B;
-    uint32_t pl[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int cs = 0;
-    for (int j = 0; j < 32; ++j) {
-      const int n = (w0 + w) * 32 + j;
-      const int v = bok ? (int)a.xq[(size_t)n * a.B + a.b0 + b] : 0;
-      cs += v;
-      const uint32_t u = (uint32_t)(uint8_t)(int8_t)v;
 #pragma unroll
-      for (int p = 0; p < 8; ++p) pl[p] |= ((u >> p) & 1u) << j;
-    }
+  for (int b = 0; b < BB; ++b) {
+    if (Q >= 4) tot[b] += __shfl_xor(tot[b], 16);
+    if (Q >= 2) tot[b] += __shfl_xor(tot[b], 32);
+  }
+  float* red = (float*)(lds + (size_t)a.W * a.wave_lds);
+  if (q == 0) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) planes[((size_t)w * BB + b) * 8 + p] = pl[p];
-    csum[(size_t)w * BB + b] = cs;
+    for (int b = 0; b < BB; ++b) red[(wv * RW + r) * BB + b] = tot[b];
   }
   __syncthreads();
-
-  const int m = rb * 64 + lane;
-  const bool valid = m < a.M;
-  const int h = min(64, a.M - rb * 64);
-  float ysum[BB];
-#pragma unroll
-  for (int b = 0; b < BB; ++b) ysum[b] = 0.0f;
-
-  for (int k = 0; k < a.K; ++k) {
-    int acck[BB];
-#pragma unroll
-    for (int b = 0; b < BB; ++b) acck[b] = 0;
-    if (valid) {
-      const uint32_t* base_k = a.bits + (size_t)k * a.plane + (size_t)rb * 64 * a.ND;
-      int cnt[BB][8];
-      int xs[BB];
-#pragma unroll
-      for (int b = 0; b < BB; ++b) {
-        xs[b] = 0;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) cnt[b][p] = 0;
-      }
-      for (int gw = 0; gw < nw; gw += 4) {
-        const int g4 = (w0 + gw) >> 2;
-        const int wg = min(4, a.ND - 4 * g4);
-        uint32_t wd[4];
-        load_tile_words(base_k + (size_t)g4 * 4 * h, lane, wg, wd);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j < wg) {
-            const uint32_t word = wd[j];
-#pragma unroll
-            for (int b = 0; b < BB; ++b) {
-              const uint32_t* pl = planes + ((size_t)(gw + j) * BB + b) * 8;
-#pragma unroll
-              for (int p = 0; p < 8; ++p) cnt[b][p] += __builtin_popcount(word & pl[p]);
-              xs[b] += csum[(size_t)(gw + j) * BB + b];
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < BB; ++b) {
-        int ones = -(cnt[b][7] << 7);
-#pragma unroll
-        for (int p = 0; p < 7; ++p) ones += cnt[b][p] << p;
-        acck[b] = 2 * ones - xs[b];
-      }
-    }
-    if (a.S == 1) {
-      if (valid) {
-        const float al = a.alpha ? a.alpha[(size_t)k * a.M + m] : 1.0f;
-#pragma unroll
-        for (int b = 0; b < BB; ++b) {
-          if (a.b0 + b < a.B) {
-            if (a.acc) a.acc[((size_t)k * a.M + m) * a.B + a.b0 + b] = acck[b];
-            ysum[b] += al * (float)acck[b];
-          }
-        }
-      }
-    } else if (valid) {
-#pragma unroll
-      for (int b = 0; b < BB; ++b) a.part[(((size_t)s * a.K + k) * a.M + m) * BB + b] = acck[b];
-    }
-  }
-
-  if (a.S > 1) {
-    if (!arrive_last(a.cnt, rb, a.S)) return;
-    if (valid) {
-      for (int k = 0; k < a.K; ++k) {
-        int sum[BB];
-#pragma unroll
-        for (int b = 0; b < BB; ++b) sum[b] = 0;
-        for (int s2 = 0; s2 < a.S; ++s2) {
-#pragma unroll
-          for (int b = 0; b < BB; ++b) sum[b] += a.part[(((size_t)s2 * a.K + k) * a.M + m) * BB + b];
-        }
-        const float al = a.alpha ? a.alpha[(size_t)k * a.M + m] : 1.0f;
-#pragma unroll
-        for (int b = 0; b < BB; ++b) {
-          if (a.b0 + b < a.B) {
-            if (a.acc) a.acc[((size_t)k * a.M + m) * a.B + a.b0 + b] = sum[b];
-            ysum[b] += al * (float)sum[b];
-          }
-        }
-      }
-    }
-    reset_counter(a.cnt, rb);
-  }
-
-  if (valid && a.y) {
-#pragma unroll
-    for (int b = 0; b < BB; ++b) {
-      if (a.b0 + b < a.B) {
-        const size_t yi = (size_t)m * a.B + a.b0 + b;
-        a.y[yi] = (a.accumulate ? a.y[yi] : 0.0f) + a.sx[a.b0 + b] * ysum[b];
-      }
+  for (int t = threadIdx.x; t < RW * BB; t += blockDim.x) {  // blockDim may be below RW * BB
+    const int rr = t / BB, b = t % BB;
+    const int mm = blockIdx.x * RW + rr;
+    if (mm < a.M && a.b0 + b < a.B) {
+      float s = 0.0f;
+      for (int w = 0; w < a.W; ++w) s += red[(w * RW + rr) * BB + b];
+      const size_t yi = (size_t)mm * a.B + a.b0 + b;
+      a.y[yi] = (a.accumulate ? a.y[yi] : 0.0f) + s;
     }
   }
 }
@@ -318,80 +204,67 @@ __global__ void __launch_bounds__(64) k_gemv_i8(GemvI8Args a) {
 static int env_int(const char* name, int dflt) {
   const char* v = std::getenv(name);
   if (!v || !*v) return dflt;
-  int r = std::atoi(v);
+  const int r = std::atoi(v);
   return r > 0 ? r : dflt;
 }
 
-static int batch_tile(int B, int K, bool i8) {
-  int bb = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : B <= 8 ? 8 : 16;
-  if (!i8) {
-    // fp32 tables: K * BB * 512 bytes per sign word must leave room for 4 words
-    while (bb > 1 && K * bb > 32) bb >>= 1;
-  }
-  return bb;
-}
-
-GemvPlan plan_gemv(int K, int M, int N, int B, bool i8) {
-  GemvPlan p{};
+ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8) {
+  ProdPlan p{};
   const int ND = N / 32;
-  p.BB = batch_tile(B, K, i8);
-  p.nchunk = (B + p.BB - 1) / p.BB;
-  p.nrb = (M + 63) / 64;
-  const int target = env_int("BSG_TARGET_WGS", 1024);
-  int S = (target + p.nrb - 1) / p.nrb;
-  S = S < 1 ? 1 : S;
-  if (p.nrb > kMaxRowBlocksSplit) S = 1;
-  const int maxS = (ND + 3) / 4;
-  S = S > maxS ? maxS : S;
-  int wb = (ND + S - 1) / S;
-  wb = (wb + 3) / 4 * 4;
-  const size_t per_word = i8 ? (size_t)p.BB * 36 : (size_t)K * p.BB * 512;
-  int wb_max = (int)(65536 / per_word) / 4 * 4;
-  if (wb_max < 4) wb_max = 4;
-  if (wb > wb_max) wb = wb_max;
-  p.wb = wb;
-  p.S = (ND + wb - 1) / wb;
-  if (p.S > 1) {
-    p.part_bytes = align_up((size_t)p.S * M * p.BB * 4 * (i8 ? K : 1), 256);
-    p.ws_bytes = kCounterBytes + p.part_bytes;
+  p.KM = K <= 2 ? 2 : K <= 4 ? 4 : 8;
+  p.BB = B <= 1 ? 1 : B <= 2 ? 2 : 4;
+  p.nlaunch = (B + p.BB - 1) / p.BB;
+  // lanes per row: the fewest that still give at least 256 workgroups
+  const int forceQ = env_int("BSG_Q", 0);
+  if (forceQ == 1 || forceQ == 2 || forceQ == 4) {
+    p.Q = forceQ;
+  } else {
+    p.Q = 4;
+    for (int qq = 1; qq <= 4; qq *= 2) {
+      if ((M + 64 / qq - 1) / (64 / qq) >= 256) {
+        p.Q = qq;
+        break;
+      }
+    }
   }
+  p.RW = 64 / p.Q;
+  const int KX = (colscale && !i8) ? K : 1;
+  // 8-word chunks (256 columns) for one batch column with at most two table
+  // sets and K <= 4; 4-word chunks otherwise
+  p.CW = (p.BB == 1 && p.KM <= 4 && (i8 || KX <= 2)) ? 8 : 4;
+  p.NWL = p.CW / p.Q;
+  p.wave_lds = i8 ? (size_t)p.CW * p.BB * 12 * 4 : (size_t)KX * p.BB * p.CW * 512;
+  const int T = (ND + p.CW - 1) / p.CW;  // chunks
+  int W = env_int("BSG_WAVES", 16);
+  W = W > 16 ? 16 : W;
+  W = W > T ? T : W;
+  const size_t red_per_wave = (size_t)p.RW * p.BB * 4 * (i8 ? p.KM : 1);
+  while (W > 1 && (size_t)W * (p.wave_lds + red_per_wave) > kMaxLds) --W;
+  p.W = W < 1 ? 1 : W;
+  p.NCH = (T + p.W - 1) / p.W;
+  p.nwg = (M + p.RW - 1) / p.RW;
+  p.lds = (size_t)p.W * (p.wave_lds + red_per_wave);
   return p;
 }
 
-hipError_t launch_gemv_f(const GemvArgs& a0, const GemvPlan& p, hipStream_t st) {
-  const int KX = a0.colscale ? a0.K : 1;
-  const size_t lds = (size_t)KX * p.BB * p.wb * 8 * 16 * sizeof(float);
-  dim3 grid(p.S, p.nrb);
-  for (int c = 0; c < p.nchunk; ++c) {
-    GemvArgs a = a0;
-    a.b0 = c * p.BB;
-    switch (p.BB) {
-      case 1: hipLaunchKernelGGL(k_gemv_f<1>, grid, dim3(64), lds, st, a); break;
-      case 2: hipLaunchKernelGGL(k_gemv_f<2>, grid, dim3(64), lds, st, a); break;
-      case 4: hipLaunchKernelGGL(k_gemv_f<4>, grid, dim3(64), lds, st, a); break;
-      case 8: hipLaunchKernelGGL(k_gemv_f<8>, grid, dim3(64), lds, st, a); break;
-      default: hipLaunchKernelGGL(k_gemv_f<16>, grid, dim3(64), lds, st, a); break;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+static hipError_t dispatch_f(const ProdArgs& a, const ProdPlan& p, hipStream_t st) {
+  switch (prod_key(p.Q, p.NWL, p.KM, p.BB)) {
+#define BSG_CASE(Q, NWL, KM, BB) \
+  case prod_key(Q, NWL, KM, BB): return launch_one(k_prod_f<Q, NWL, KM, BB>, p, a, st);
+    BSG_PROD_INSTANCES(BSG_CASE)
+#undef BSG_CASE
+    default: return hipErrorInvalidConfiguration;
   }
-  return hipSuccess;
 }
 
-hipError_t launch_gemv_i8(const GemvI8Args& a0, const GemvPlan& p, hipStream_t st) {
-  const size_t lds = (size_t)p.wb * p.BB * 9 * sizeof(uint32_t);
-  dim3 grid(p.S, p.nrb);
-  for (int c = 0; c < p.nchunk; ++c) {
-    GemvI8Args a = a0;
+hipError_t launch_prod_f(const ProdArgs& a0, const ProdPlan& p, hipStream_t st) {
+  for (int c = 0; c < p.nlaunch; ++c) {
+    ProdArgs a = a0;
     a.b0 = c * p.BB;
-    switch (p.BB) {
-      case 1: hipLaunchKernelGGL(k_gemv_i8<1>, grid, dim3(64), lds, st, a); break;
-      case 2: hipLaunchKernelGGL(k_gemv_i8<2>, grid, dim3(64), lds, st, a); break;
-      case 4: hipLaunchKernelGGL(k_gemv_i8<4>, grid, dim3(64), lds, st, a); break;
-      case 8: hipLaunchKernelGGL(k_gemv_i8<8>, grid, dim3(64), lds, st, a); break;
-      default: hipLaunchKernelGGL(k_gemv_i8<16>, grid, dim3(64), lds, st, a); break;
-    }
-    hipError_t e = hipGetLastError();
+    a.W = p.W;
+    a.NCH = p.NCH;
+    a.wave_lds = (uint32_t)p.wave_lds;
+    const hipError_t e = dispatch_f(a, p, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -1,0 +1,169 @@
+// Sign product with int8 activations for gfx950, exact in int32:
+//
+//   acc_k[m,b] = sum_n (2 bit_k(m,n) - 1) xq[n,b]
+//   y[m,b] (= or +=) sx[b] * sum_k alpha_k[m] acc_k[m,b]
+//
+// With the two's-complement bit planes P_p of xq over the 32 columns of a
+// sign word, sum_{bit=1} xq = sum_{p<7} 2^p popcount(word & P_p)
+// - 128 popcount(word & P_7), and sum_n (2 bit - 1) xq = 2 sum_{bit=1} xq -
+// sum_n xq: per 32 weights 8 AND and 8 popcount-accumulate, no table.  Each
+// wavefront makes the planes of its chunk with 8 ballots per two sign words
+// and stores them as [word][batch column][8 planes, column sum, 3 pad]
+// (48 bytes, two 16-byte reads).  The work decomposition is the one of the
+// float path (bsg_gemv.hip): complete rows per workgroup, no cross-workgroup
+// reduction, fixed summation order.
+#include "bsg_prod.h"
+
+namespace bsg {
+
+template <int Q, int NWL, int KM, int BB>
+__global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
+  constexpr int RW = 64 / Q;
+  constexpr int CW = Q * NWL;
+  extern __shared__ __align__(16) char lds[];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int q = lane / RW;
+  const int r = lane % RW;
+  const int m = blockIdx.x * RW + r;
+  const bool valid = m < a.M;
+  uint32_t* pl = (uint32_t*)(lds + (size_t)wv * a.wave_lds);
+
+  int cnt[KM][BB][8];
+  int xs[BB];
+#pragma unroll
+  for (int b = 0; b < BB; ++b) {
+    xs[b] = 0;
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+#pragma unroll
+      for (int p = 0; p < 8; ++p) cnt[k][b][p] = 0;
+  }
+
+  uint32_t cur[KM][NWL], nxt[KM][NWL];
+  load_chunk<KM, NWL>(a, valid, m, wv * a.NCH * CW + q * NWL, cur);
+
+  for (int c = 0; c < a.NCH; ++c) {
+    const int cw0 = (wv * a.NCH + c) * CW;
+    if (c + 1 < a.NCH) load_chunk<KM, NWL>(a, valid, m, cw0 + CW + q * NWL, nxt);
+
+    // ---- bit planes: one ballot over 64 lanes covers two sign words
+    for (int u = 0; u < CW / 2; ++u) {
+      const int n = (cw0 + 2 * u) * 32 + lane;
+#pragma unroll
+      for (int b = 0; b < BB; ++b) {
+        const int v = (n < a.N && a.b0 + b < a.B) ? (int)a.xq[(size_t)n * a.B + a.b0 + b] : 0;
+        uint32_t lo[8], hi[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const unsigned long long bal = __ballot((v >> p) & 1);
+          lo[p] = (uint32_t)bal;
+          hi[p] = (uint32_t)(bal >> 32);
+        }
+        if (lane == 0 || lane == 32) {
+          const int wl = 2 * u + (lane == 32 ? 1 : 0);
+          uint32_t* dst = pl + ((size_t)wl * BB + b) * 12;
+          int sum = 0;
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            const uint32_t bits = lane == 0 ? lo[p] : hi[p];
+            dst[p] = bits;
+            sum += (p == 7 ? -128 : (1 << p)) * __builtin_popcount(bits);
+          }
+          dst[8] = (uint32_t)sum;
+        }
+      }
+    }
+    __syncthreads();
+
+    const int lw0 = cw0 + q * NWL;
+#pragma unroll
+    for (int j = 0; j < NWL; ++j) {
+      if (valid && lw0 + j < a.ND) {
+#pragma unroll
+        for (int b = 0; b < BB; ++b) {
+          const uint32_t* src = pl + ((size_t)(q * NWL + j) * BB + b) * 12;
+          const uint4 P0 = *(const uint4*)src;
+          const uint4 P1 = *(const uint4*)(src + 4);
+          const uint32_t P[8] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
+          xs[b] += (int)src[8];
+#pragma unroll
+          for (int k = 0; k < KM; ++k) {
+            if (k < a.K) {
+#pragma unroll
+              for (int p = 0; p < 8; ++p) cnt[k][b][p] += __builtin_popcount(cur[k][j] & P[p]);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (c + 1 < a.NCH) {
+#pragma unroll
+      for (int k = 0; k < KM; ++k)
+#pragma unroll
+        for (int j = 0; j < NWL; ++j) cur[k][j] = nxt[k][j];
+    }
+  }
+
+  // exact int32 per (base, batch column): this lane, the Q lanes of the row,
+  // then the W wavefronts
+  int* red = (int*)(lds + (size_t)a.W * a.wave_lds);
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+#pragma unroll
+    for (int b = 0; b < BB; ++b) {
+      int ones = -(cnt[k][b][7] << 7);
+#pragma unroll
+      for (int p = 0; p < 7; ++p) ones += cnt[k][b][p] << p;
+      int v = 2 * ones - xs[b];
+      if (Q >= 4) v += __shfl_xor(v, 16);
+      if (Q >= 2) v += __shfl_xor(v, 32);
+      if (q == 0 && k < a.K) red[((wv * RW + r) * KM + k) * BB + b] = v;
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < RW * BB; t += blockDim.x) {  // blockDim may be below RW * BB
+    const int rr = t / BB, b = t % BB;
+    const int mm = blockIdx.x * RW + rr;
+    if (mm < a.M && a.b0 + b < a.B) {
+      float ysum = 0.0f;
+      for (int k = 0; k < a.K; ++k) {
+        int s = 0;
+        for (int w = 0; w < a.W; ++w) s += red[((w * RW + rr) * KM + k) * BB + b];
+        if (a.acc) a.acc[((size_t)k * a.M + mm) * a.B + a.b0 + b] = s;
+        if (a.y) ysum += (a.alpha ? a.alpha[(size_t)k * a.M + mm] : 1.0f) * (float)s;
+      }
+      if (a.y) {
+        const size_t yi = (size_t)mm * a.B + a.b0 + b;
+        a.y[yi] = (a.accumulate ? a.y[yi] : 0.0f) + a.sx[a.b0 + b] * ysum;
+      }
+    }
+  }
+}
+
+static hipError_t dispatch_i8(const ProdArgs& a, const ProdPlan& p, hipStream_t st) {
+  switch (prod_key(p.Q, p.NWL, p.KM, p.BB)) {
+#define BSG_CASE(Q, NWL, KM, BB) \
+  case prod_key(Q, NWL, KM, BB): return launch_one(k_prod_i8<Q, NWL, KM, BB>, p, a, st);
+    BSG_PROD_INSTANCES(BSG_CASE)
+#undef BSG_CASE
+    default: return hipErrorInvalidConfiguration;
+  }
+}
+
+hipError_t launch_prod_i8(const ProdArgs& a0, const ProdPlan& p, hipStream_t st) {
+  for (int c = 0; c < p.nlaunch; ++c) {
+    ProdArgs a = a0;
+    a.b0 = c * p.BB;
+    a.W = p.W;
+    a.NCH = p.NCH;
+    a.wave_lds = (uint32_t)p.wave_lds;
+    const hipError_t e = dispatch_i8(a, p, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace bsg

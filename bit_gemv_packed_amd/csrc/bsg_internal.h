@@ -14,13 +14,7 @@ constexpr int kRowBlock = 64;   // rows per layout tile = lanes per wavefront
 constexpr int kGroupWords = 4;  // words per layout tile (one 16-byte load per lane)
 constexpr int kMaxK = 8;
 constexpr int kMaxB = 64;
-// Every workspace starts with this many bytes of arrival counters (one per
-// 64-row block), zero-filled once by the caller and left zero by every
-// completed call; partial sums and other scratch follow.  The fixed size
-// keeps the counter area in the same place for every shape, so one
-// workspace serves calls of any size.
-constexpr size_t kCounterBytes = 65536;
-constexpr int kMaxRowBlocksSplit = (int)(kCounterBytes / 4);
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
 // Words of one base in the device layout: M*ND rounded up to 64 words.
 __host__ __device__ inline size_t plane_words(int M, int ND) {
@@ -56,47 +50,45 @@ __device__ inline float load_x(const void* x, int dt, size_t i) {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Launch plan of the sign products: 64-row blocks (one wavefront each) times
-// S column splits of wb words; each split builds its own activation tables.
-struct GemvPlan {
-  int BB;    // batch columns per launch (1, 2, 4, 8 or 16)
-  int S;     // column splits
-  int wb;    // words per split (multiple of 4, except that the last split may be short)
-  int nrb;   // 64-row blocks
-  int nchunk;// launches over batch chunks of BB
-  size_t part_bytes;  // partial sums (S > 1)
-  size_t ws_bytes;    // kCounterBytes + part_bytes when S > 1, else 0
+// Launch plan of the sign products (bsg_gemv.hip).  A workgroup owns RW =
+// 64/Q full rows; Q lanes of a wavefront share a row and each covers 1/Q of
+// the wavefront's column chunk; W wavefronts split the input dimension into
+// chunks of CW = Q*NWL sign words, NCH chunks each.  No reduction crosses
+// workgroups.
+struct ProdPlan {
+  int Q;       // lanes per row: 1, 2 or 4
+  int NWL;     // sign words per lane per chunk and base
+  int KM;      // bases unrolled (K <= KM)
+  int BB;      // batch columns per launch
+  int CW;      // words per chunk (Q * NWL)
+  int RW;      // rows per workgroup (64 / Q)
+  int W;       // wavefronts per workgroup
+  int NCH;     // chunks per wavefront
+  int nwg;     // workgroups
+  int nlaunch; // launches over batch chunks of BB columns
+  size_t wave_lds;  // LDS bytes per wavefront (tables or bit planes)
+  size_t lds;       // LDS bytes per workgroup
 };
 
-GemvPlan plan_gemv(int K, int M, int N, int B, bool int8_mode);
+ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool int8_mode);
 
-struct GemvArgs {
+struct ProdArgs {
   const uint32_t* bits;
-  const float* alpha;        // fp32 [K][M] or NULL
-  const uint16_t* alpha_h;   // fp16 [K][M] or NULL (alpha == NULL && alpha_h == NULL -> 1)
-  const uint16_t* colscale;  // fp16 [K][N] or NULL
-  const void* x;             // [N][B]
-  float* y;                  // [M][B]
-  float* part;               // [S][M][BB] partials
-  unsigned* cnt;             // [nrb] arrival counters
+  const float* alpha;        // fp32 [K][M], or NULL
+  const uint16_t* alpha_h;   // fp16 [K][M], or NULL (both NULL: 1)
+  const uint16_t* colscale;  // fp16 [K][N], or NULL
+  const void* x;             // [N][B] of dtype xdt (float path)
+  const int8_t* xq;          // [N][B] (int8 path)
+  const float* sx;           // [B] (int8 path)
+  int32_t* acc;              // [K][M][B] or NULL (int8 path)
+  float* y;                  // [M][B] or NULL (int8 path)
   size_t plane;
-  int K, M, N, ND, B, b0, xdt, accumulate, S, wb;
+  int K, M, N, ND, B, b0, xdt, accumulate, W, NCH;
+  int xvec;                  // x 16-byte and colscale 8-byte aligned: vector loads
+  uint32_t wave_lds;
 };
 
-struct GemvI8Args {
-  const uint32_t* bits;
-  const float* alpha;
-  const int8_t* xq;          // [N][B]
-  const float* sx;           // [B]
-  int32_t* acc;              // [K][M][B] or NULL
-  float* y;                  // [M][B] or NULL
-  int32_t* part;             // [S][K][M][BB]
-  unsigned* cnt;
-  size_t plane;
-  int K, M, N, ND, B, b0, accumulate, S, wb;
-};
-
-hipError_t launch_gemv_f(const GemvArgs& a, const GemvPlan& p, hipStream_t s);
-hipError_t launch_gemv_i8(const GemvI8Args& a, const GemvPlan& p, hipStream_t s);
+hipError_t launch_prod_f(const ProdArgs& a, const ProdPlan& p, hipStream_t s);
+hipError_t launch_prod_i8(const ProdArgs& a, const ProdPlan& p, hipStream_t s);
 
 }  // namespace bsg

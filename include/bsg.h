@@ -98,17 +98,9 @@ BSG_API size_t bsg_layout_words(int K, int M, int N);
  * -1 if an index is out of range.  A pure host function. */
 BSG_API int64_t bsg_layout_word_offset(int K, int M, int N, int k, int m, int w);
 
-/* Device workspace bytes needed by bs_gemv / bs_gemv_i8 for these sizes
- * (0 when the launch plan needs none).  Every workspace starts with a
- * 64 KiB area of arrival counters (one per 64-row block) followed by the
- * per-split partial sums.  The counter area must be zero-filled before the
- * workspace is first used; every completed call leaves it zero again, so
- * one workspace serves calls of any size in sequence.  Calls that overlap
- * in time must not share a workspace. */
-BSG_API size_t bsg_gemv_workspace_bytes(int K, int M, int N, int B);
-
-/* Device workspace bytes needed by binlr_apply (the counter area, z, and
- * the partial sums of its two sign products); same zero-fill rule. */
+/* Device workspace bytes needed by binlr_apply: z = alpha_r (.) (V x), fp32
+ * [r][B].  No initial contents are required.  Calls that overlap in time
+ * must not share a workspace. */
 BSG_API size_t bsg_binlr_workspace_bytes(int r, int M, int N, int B);
 
 /* ------------------------------------------------------------------ */
@@ -206,15 +198,14 @@ BSG_API bsg_status bsg_layout_to_logical(const uint32_t* bits, int K, int M, int
  *   x         (device) [N][B] (element (n, b) at n*B + b) of dtype x_dtype
  *   y         (device) fp32 [M][B]; overwritten when accumulate == 0,
  *             added to otherwise
- *   workspace (device) >= bsg_gemv_workspace_bytes(K, M, N, B) (may be NULL
- *             when that is 0); zero-filled before first use
- * 1 <= K <= 8, 1 <= B <= 64.  Accumulation is fp32; the result is within
+ * 1 <= K <= 8, 1 <= B <= 64.  Accumulation is fp32 in a fixed order (the
+ * result does not depend on scheduling); it is within
  * 2e-3 * sum_k |alpha_k[m]| * sum_n |c_k[n] x[n,b]| of the exact value.
+ * Needs no workspace: every output row is reduced inside one workgroup.
  */
 BSG_API bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const float* alpha,
                    const uint16_t* colscale, const void* x, int x_dtype, int B,
-                   float* y, int accumulate, void* workspace, size_t workspace_bytes,
-                   void* stream);
+                   float* y, int accumulate, void* stream);
 
 /*
  * bs_gemv_i8 -- the same product with int8 activations, exact in integers:
@@ -227,8 +218,7 @@ BSG_API bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const floa
  */
 BSG_API bsg_status bs_gemv_i8(const uint32_t* bits, int K, int M, int N, const float* alpha,
                       const int8_t* xq, const float* sx, int B, int32_t* acc,
-                      float* y, int accumulate, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      float* y, int accumulate, void* stream);
 
 /*
  * binlr_apply -- binary low-rank correction (BiLoCo "The core idea"):

@@ -80,16 +80,14 @@ def test_layout_formula_matches_oracle(K, M, N):
 
 
 def test_workspace_sizes():
-    # the 4096x4096 two-base product splits its input dimension: needs a workspace
-    assert bsg.gemv_workspace_bytes(2, 4096, 4096, 1) >= 65536
-    assert bsg.gemv_workspace_bytes(0, 4096, 4096, 1) == 0
-    assert bsg.binlr_workspace_bytes(512, 5120, 5120, 1) >= 65536 + 512 * 4
+    assert bsg.binlr_workspace_bytes(512, 5120, 5120, 1) >= 512 * 4
+    assert bsg.binlr_workspace_bytes(512, 5120, 5120, 16) >= 512 * 16 * 4
     assert bsg.binlr_workspace_bytes(500, 5120, 5120, 1) == 0
     assert bsg.lib().bsq_pack_workspace_bytes(100, 64) >= 100 * 64 * 8
 
 
-def _gemv(bits=A16, K=2, M=128, N=256, alpha=A16b, cs=None, x=A16c, dt=2, B=1, y=A16d, acc=0, ws=None, wsb=0):
-    return bsg.lib().bs_gemv(bits, K, M, N, alpha, cs, x, dt, B, y, acc, ws, wsb, None)
+def _gemv(bits=A16, K=2, M=128, N=256, alpha=A16b, cs=None, x=A16c, dt=2, B=1, y=A16d, acc=0):
+    return bsg.lib().bs_gemv(bits, K, M, N, alpha, cs, x, dt, B, y, acc, None)
 
 
 @fake_ptrs
@@ -111,11 +109,7 @@ def test_bs_gemv_validation():
     assert _gemv(alpha=A16b + 2) == EALIGN
     assert _gemv(x=A16c + 1, dt=2) == EALIGN
     assert _gemv(cs=A16 + 1) == EALIGN
-    # needs a workspace at this size
-    assert _gemv(K=2, M=4096, N=4096) == EWS
-    need = bsg.gemv_workspace_bytes(2, 4096, 4096, 1)
-    assert _gemv(K=2, M=4096, N=4096, ws=0x500000, wsb=16) == EWS
-    assert _gemv(K=2, M=4096, N=4096, ws=0x500008, wsb=need) == EALIGN
+    assert _gemv(y=A16d + 2) == EALIGN
 
 
 @fake_ptrs
@@ -123,7 +117,7 @@ def test_bs_gemv_i8_validation():
     L = bsg.lib()
     f = lambda **kw: L.bs_gemv_i8(kw.get("bits", A16), kw.get("K", 2), kw.get("M", 128), kw.get("N", 256),
                                   kw.get("alpha", A16b), kw.get("xq", A16c), kw.get("sx", A16d), kw.get("B", 1),
-                                  kw.get("acc", A16), kw.get("y", None), 0, None, 0, None)
+                                  kw.get("acc", A16), kw.get("y", None), 0, None)
     assert f(N=48) == ESHAPE
     assert f(N=(1 << 24) + 32) == ESHAPE
     assert f(acc=None, y=None) == ENULL
@@ -137,6 +131,7 @@ def test_binlr_and_salient_validation():
     L = bsg.lib()
     assert L.binlr_apply(A16, A16b, A16c, 500, 64, 64, A16d, 2, 1, A16, None, 0, None) == ESHAPE
     assert L.binlr_apply(A16, A16b, A16c, 32, 64, 64, A16d, 2, 1, A16, None, 0, None) == EWS
+    assert L.binlr_apply(A16, A16b, A16c, 32, 64, 64, A16d, 2, 1, A16, 0x500000, 64, None) == EWS
     assert L.binlr_apply(None, A16b, A16c, 32, 64, 64, A16d, 2, 1, A16, None, 0, None) == ENULL
     assert L.binlr_apply(A16, A16b, A16c, 32, 64, 64, A16d, 9, 1, A16, None, 0, None) == EDTYPE
     assert L.salient_int8_apply(A16, 3, A16b, A16c, 64, 64, A16d, 2, 1, None, None) == ENULL

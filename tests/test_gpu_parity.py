@@ -56,6 +56,11 @@ GEMV_CASES = [
     (8, 65, 256, 1, True, "f32", "normal"),
     (4, 2000, 768, 8, False, "bf16", "normal"),
     (2, 5, 14336, 1, False, "bf16", "normal"),
+    (3, 300, 544, 1, True, "bf16", "normal"),
+    (4, 130, 1024, 2, True, "f32", "normal"),
+    (5, 77, 320, 3, False, "bf16", "normal"),
+    (2, 17000, 256, 1, True, "bf16", "normal"),
+    (1, 9000, 96, 2, False, "f16", "normal"),
 ]
 
 
@@ -86,6 +91,34 @@ def test_bs_gemv_matches_oracle(case):
     y2 = bsg.bs_gemv(bits, K, M, N, ad, xd, colscale=cd)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+
+
+# Every kernel instance and the multi-chunk loop, by forcing the lanes per
+# row (Q) and the wavefronts per workgroup (fewer wavefronts -> more chunks).
+FORCED = [(q, w) for q in (1, 2, 4) for w in (1, 3, 16)]
+FORCED_SHAPES = [(1, 200, 1056, 1, False, "bf16", "normal"), (2, 130, 2080, 1, True, "bf16", "normal"),
+                 (4, 70, 800, 1, True, "f32", "normal"), (3, 90, 544, 2, False, "bf16", "normal"),
+                 (6, 65, 256, 4, False, "f16", "normal"), (2, 64, 4096, 3, True, "bf16", "student_t3")]
+
+
+@pytest.mark.parametrize("qw", FORCED, ids=lambda c: "Q%d_W%d" % c)
+def test_bs_gemv_every_instance(qw, monkeypatch):
+    monkeypatch.setenv("BSG_Q", str(qw[0]))
+    monkeypatch.setenv("BSG_WAVES", str(qw[1]))
+    for case in FORCED_SHAPES:
+        K, M, N, B, cs, dt, dist = case
+        say("bs_gemv forced", qw, case)
+        L, alpha, csb, x = _gemv_inputs(case)
+        bits = _layout(L, K, M, N)
+        y = bsg.bs_gemv(bits, K, M, N, to_dev(alpha), x_dev(x, dt), colscale=f16_dev(csb) if cs else None)
+        torch.cuda.synchronize()
+        ref = oracle.sign_gemv(L, K, M, N, alpha, x, csb)
+        check_close(y.cpu().numpy(), ref, oracle.tolerance(x, alpha=alpha, colscale_f16=csb), "forced %s %s" % (qw, case))
+        # int8 mode through the same decomposition
+        xq, sx = oracle.quantize_i8(x)
+        acc, _ = bsg.bs_gemv_i8(bits, K, M, N, to_dev(alpha), to_dev(xq), to_dev(sx), want_y=False)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy().astype(np.int64), oracle.sign_gemv_i8(L, K, M, N, xq))
 
 
 def test_bs_gemv_accumulate_and_negation():
