@@ -16,18 +16,20 @@
 
 namespace bsg {
 
-template <int Q, int NWL, int KM, int BB>
+template <int Q, int NWL, int KM, int BB, int XM>
 __global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
   constexpr int RW = 64 / Q;
   constexpr int CW = Q * NWL;
   extern __shared__ __align__(16) char lds[];
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wavefront index (uniform)
   const int q = lane / RW;
   const int r = lane % RW;
   const int m = blockIdx.x * RW + r;
   const bool valid = m < a.M;
+  const int mload = valid ? m : a.M - 1;  // rows beyond M load a valid row; their sums are dropped
+  const int ndfull = a.ND & ~3;
   uint32_t* pl = (uint32_t*)(lds + (size_t)wv * a.wave_lds);
 
   int cnt[KM][BB][8];
@@ -42,11 +44,11 @@ __global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
   }
 
   uint32_t cur[KM][NWL], nxt[KM][NWL];
-  load_chunk<KM, NWL>(a, valid, m, wv * a.NCH * CW + q * NWL, cur);
+  load_chunk<KM, NWL>(a, wv * a.NCH * CW + CW <= ndfull, mload, wv * a.NCH * CW + q * NWL, cur);
 
   for (int c = 0; c < a.NCH; ++c) {
     const int cw0 = (wv * a.NCH + c) * CW;
-    if (c + 1 < a.NCH) load_chunk<KM, NWL>(a, valid, m, cw0 + CW + q * NWL, nxt);
+    if (c + 1 < a.NCH) load_chunk<KM, NWL>(a, cw0 + 2 * CW <= ndfull, mload, cw0 + CW + q * NWL, nxt);
 
     // ---- bit planes: one ballot over 64 lanes covers two sign words
     for (int u = 0; u < CW / 2; ++u) {
@@ -80,7 +82,7 @@ __global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
     const int lw0 = cw0 + q * NWL;
 #pragma unroll
     for (int j = 0; j < NWL; ++j) {
-      if (valid && lw0 + j < a.ND) {
+      if (lw0 + j < a.ND) {
 #pragma unroll
         for (int b = 0; b < BB; ++b) {
           const uint32_t* src = pl + ((size_t)(q * NWL + j) * BB + b) * 12;
@@ -90,7 +92,7 @@ __global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
           xs[b] += (int)src[8];
 #pragma unroll
           for (int k = 0; k < KM; ++k) {
-            if (k < a.K) {
+            if (base_active<KM>(a, k)) {
 #pragma unroll
               for (int p = 0; p < 8; ++p) cnt[k][b][p] += __builtin_popcount(cur[k][j] & P[p]);
             }
@@ -144,10 +146,10 @@ __global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
 }
 
 static hipError_t dispatch_i8(const ProdArgs& a, const ProdPlan& p, hipStream_t st) {
-  switch (prod_key(p.Q, p.NWL, p.KM, p.BB)) {
-#define BSG_CASE(Q, NWL, KM, BB) \
-  case prod_key(Q, NWL, KM, BB): return launch_one(k_prod_i8<Q, NWL, KM, BB>, p, a, st);
-    BSG_PROD_INSTANCES(BSG_CASE)
+  switch (prod_key(p.Q, p.NWL, p.KM, p.BB, 0)) {
+#define BSG_CASE(Q, NWL, KM, BB, XM) \
+  case prod_key(Q, NWL, KM, BB, XM): return launch_one(k_prod_i8<Q, NWL, KM, BB, XM>, p, a, st);
+    BSG_PROD_I8_INSTANCES(BSG_CASE)
 #undef BSG_CASE
     default: return hipErrorInvalidConfiguration;
   }

@@ -58,7 +58,8 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct ProdPlan {
   int Q;       // lanes per row: 1, 2 or 4
   int NWL;     // sign words per lane per chunk and base
-  int KM;      // bases unrolled (K <= KM)
+  int KM;      // bases unrolled: K itself for K <= 4, else 8
+  int XM;      // float kernel activation path: 0 generic, 1 / 2 one aligned bf16 / fp16 batch column
   int BB;      // batch columns per launch
   int CW;      // words per chunk (Q * NWL)
   int RW;      // rows per workgroup (64 / Q)
