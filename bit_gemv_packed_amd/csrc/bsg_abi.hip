@@ -221,10 +221,9 @@ bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uin
   hipStream_t st = (hipStream_t)stream;
   float* z = (float*)workspace;
 
-  // z = alpha_r (.) (V x): a one-base sign product with fp16 row scales
+  // z' = V x: a one-base sign product with unit row scales
   ProdArgs v{};
   v.bits = V_bits;
-  v.alpha_h = alpha_r;
   v.x = x;
   v.y = z;
   v.plane = plane_words(r, N / 32);
@@ -239,9 +238,12 @@ bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uin
   hipError_t e = launch_prod_f(v, plan_prod(1, r, N, B, false, false), st);
   if (e != hipSuccess) return BSG_ERR_HIP;
 
-  // y += U z: a one-base sign product over the r ranks with unit row scales
+  // y += U (alpha_r (.) z'): a one-base sign product over the r ranks with
+  // unit row scales and alpha_r as its column scales (folded into z' when the
+  // kernel stages its activations)
   ProdArgs u{};
   u.bits = U_bits;
+  u.colscale = alpha_r;
   u.x = z;
   u.y = y;
   u.plane = plane_words(M, r / 32);
@@ -253,7 +255,7 @@ bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uin
   u.xdt = BSG_F32;
   u.accumulate = 1;
   u.xvec = 1;
-  return hip_status(launch_prod_f(u, plan_prod(1, M, r, B, false, false), st));
+  return hip_status(launch_prod_f(u, plan_prod(1, M, r, B, true, false), st));
 }
 
 bsg_status salient_int8_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s_f16, int M, int N,

@@ -15,7 +15,10 @@
 // pattern as the table address; Sec. 3.2 Stage 1: fold the column scale into
 // x while building the table).  Sub-vectors are 4 columns wide: 16 fp32
 // entries per table.  Each wavefront builds the tables of its own chunk in
-// its own LDS region, laid out [step][quarter][16 entries] with 16 pad bytes
+// its own LDS region, so the chunk loop has no workgroup barrier: the
+// wavefronts drift apart and one's memory wait overlaps another's lookups
+// (the only barrier precedes the final cross-wavefront sum).  Tables are
+// laid out [step][quarter][16 entries] with 16 pad bytes
 // after each step row: at every lookup the lanes of a quarter read one
 // 64-byte table and the Q tables of one instruction occupy disjoint bank
 // groups, and the pad staggers the tables that different lanes write at
@@ -35,17 +38,23 @@ namespace bsg {
 typedef __attribute__((address_space(3))) const float lds_cf32;
 __device__ inline float lds_f32(uint32_t addr) { return *(lds_cf32*)(uintptr_t)addr; }
 
-__device__ inline float row_alpha(const ProdArgs& a, int k, int m) {
-  if (a.alpha) return a.alpha[(size_t)k * a.M + m];
-  if (a.alpha_h) return f16_bits_to_float(a.alpha_h[(size_t)k * a.M + m]);
-  return 1.0f;
+// Resources of the activations, column scales and row scales (size 0 when
+// absent: their loads then read 0).
+struct ActSrc {
+  rsrc_t x, c, al;
+};
+__device__ inline ActSrc act_src(const ProdArgs& a) {
+  ActSrc s;
+  s.x = make_rsrc(a.x, (size_t)a.N * a.B * (a.xdt == BSG_F32 ? 4 : 2));
+  s.c = make_rsrc(a.colscale, a.colscale ? (size_t)a.K * a.N * 2 : 0);
+  s.al = make_rsrc(a.alpha, a.alpha ? (size_t)a.K * a.M * 4 : 0);
+  return s;
 }
 
 // Raw activation bits -> fp32 (fp32 bits, or a bf16 / fp16 pattern in the low half).
 __device__ inline float decode_x(uint32_t raw, int xdt) {
-  if (xdt == BSG_F32) return __uint_as_float(raw);
-  if (xdt == BSG_BF16) return __uint_as_float(raw << 16);
-  return f16_bits_to_float((uint16_t)raw);
+  const float h = f16_bits_to_float((uint16_t)raw);
+  return xdt == BSG_F32 ? __uint_as_float(raw) : xdt == BSG_BF16 ? __uint_as_float(raw << 16) : h;
 }
 
 // Activations and column scales of one 4-column group, as raw bits; loaded
@@ -58,50 +67,48 @@ struct ActRaw {
 };
 
 // XM = 1 (bf16) and 2 (fp16): one batch column of 16-bit activations, x
-// 16-byte and column scales 8-byte aligned: one 8-byte load of x and one per
-// base of scales, straight-line (without column scales the scale loads read
-// x instead and are ignored).  XM = 0: any batch, dtype and alignment,
-// element loads.
+// 16-byte and column scales 8-byte aligned: one 8-byte load of x (kept
+// packed) and one per base of scales.  XM = 0: any batch, dtype and
+// alignment, two 16-bit loads per element (the second is the high half of
+// an fp32 element, unused otherwise), 16-bit loads of the scales.  Columns at
+// or beyond N read 0.
 template <int KM, int BB, int XM>
-__device__ inline void fetch_act(const ProdArgs& a, bool cs, int n0, ActRaw<KM, BB>& r) {
-  const int nc = n0 < a.N ? n0 : 0;  // columns beyond N load column 0 (the build zeroes them)
+__device__ inline void fetch_act(const ProdArgs& a, const ActSrc& src, int n0, ActRaw<KM, BB>& r) {
   if (XM != 0) {
-    const uint2 v = *(const uint2*)((const uint16_t*)a.x + nc);
-    r.x[0][0] = v.x & 0xffffu;
-    r.x[0][1] = v.x >> 16;
-    r.x[0][2] = v.y & 0xffffu;
-    r.x[0][3] = v.y >> 16;
-    const uint16_t* cbase = cs ? a.colscale : (const uint16_t*)a.x;
-    const size_t cstride = cs ? (size_t)a.N : 0;
+    const uint2 v = ld64(src.x, (uint32_t)n0 * 2u);
+    r.x[0][0] = v.x;
+    r.x[0][1] = v.y;
 #pragma unroll
     for (int k = 0; k < KM; ++k)
-      if (base_active<KM>(a, k)) r.c[k] = *(const uint2*)(cbase + (size_t)k * cstride + nc);
+      if (base_active<KM>(a, k)) r.c[k] = ld64(src.c, (uint32_t)(k * a.N + n0) * 2u);
   } else {
+    const uint32_t esz = a.xdt == BSG_F32 ? 4u : 2u;
 #pragma unroll
     for (int b = 0; b < BB; ++b) {
       const int bb = a.b0 + b < a.B ? a.b0 + b : a.B - 1;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const size_t i = (size_t)(nc + j) * a.B + bb;
-        r.x[b][j] = a.xdt == BSG_F32 ? __float_as_uint(((const float*)a.x)[i]) : (uint32_t)((const uint16_t*)a.x)[i];
+        const uint32_t off = (uint32_t)((n0 + j) * a.B + bb) * esz;
+        const uint32_t lo = ld16(src.x, off), hi = ld16(src.x, off + 2);
+        r.x[b][j] = esz == 4 ? (lo | (hi << 16)) : lo;
       }
     }
-    if (cs) {
 #pragma unroll
-      for (int k = 0; k < KM; ++k) {
-        if (base_active<KM>(a, k)) {
-          const uint16_t* p = a.colscale + (size_t)k * a.N + nc;
-          r.c[k] = make_uint2((uint32_t)p[0] | ((uint32_t)p[1] << 16), (uint32_t)p[2] | ((uint32_t)p[3] << 16));
-        }
+    for (int k = 0; k < KM; ++k) {
+      if (base_active<KM>(a, k)) {
+        const uint32_t off = (uint32_t)(k * a.N + n0) * 2u;
+        r.c[k] = make_uint2(ld16(src.c, off) | (ld16(src.c, off + 2) << 16),
+                            ld16(src.c, off + 4) | (ld16(src.c, off + 6) << 16));
       }
     }
   }
 }
 
-// Lookups of one chunk: acc[k][b] += table entry of each 4-bit slice.
-// FULL: every word of the chunk exists (no per-word guard).
-template <int Q, int NWL, int KM, int BB, bool FULL>
-__device__ inline void lookup_chunk(const ProdArgs& a, const char* lds, uint32_t wbase_lds, bool cs, int q, int lw0,
+// Lookups of one chunk: acc[k][b] += table entry of each 4-bit slice.  Words
+// beyond ND are zero words (padding) or read 0 (beyond the row block) and
+// their columns' tables are zero, so they add +-0 and need no guard.
+template <int Q, int NWL, int KM, int BB>
+__device__ inline void lookup_chunk(const ProdArgs& a, const char* lds, uint32_t wbase_lds, bool cs, int q,
                                     const uint32_t (&cur)[KM][NWL], float (&acc)[KM][BB]) {
   constexpr uint32_t ROWB = Q * 64 + 16;             // bytes of one step row of tables
   constexpr uint32_t REG = NWL * 8 * ROWB;           // bytes of one (base, batch column) table set
@@ -112,7 +119,7 @@ __device__ inline void lookup_chunk(const ProdArgs& a, const char* lds, uint32_t
           (uint32_t)(uintptr_t)(lds + wbase_lds + (uint32_t)(cs ? k : 0) * BB * REG + (uint32_t)q * 64);
 #pragma unroll
       for (int j = 0; j < NWL; ++j) {
-        if (FULL || lw0 + j < a.ND) {
+        {
           const uint32_t word = cur[k][j];
           const uint32_t rl = __builtin_amdgcn_alignbit(word, word, 30) & 0x3c3c3c3cu;  // even slices * 4
           const uint32_t rr = __builtin_amdgcn_alignbit(word, word, 2) & 0x3c3c3c3cu;   // odd slices * 4
@@ -131,14 +138,25 @@ __device__ inline void lookup_chunk(const ProdArgs& a, const char* lds, uint32_t
             for (int b = 0; b < BB; ++b)
               acc[k][b] += lds_f32(ad[n] + (uint32_t)(j * 8 + n) * ROWB + (uint32_t)b * REG);
           }
+          // finish this word's adds here: left free, the compiler sinks the
+          // add chains to the end of the loop body and keeps every table
+          // entry of the chunk live, which exhausts the registers
+#pragma unroll
+          for (int b = 0; b < BB; ++b) asm volatile("" : "+v"(acc[k][b]));
         }
       }
     }
   }
 }
 
+// Register budget.  With one or two bases, one batch column and Q >= 2 the
+// tables of a 16-wavefront workgroup take at most half the LDS, and the
+// kernel is held to 64 VGPRs (8 wavefronts per SIMD) so that two such
+// workgroups share a compute unit.  Instances with KM * BB >= 8 keep more
+// sums in registers and run at most 8 wavefronts per workgroup.
 template <int Q, int NWL, int KM, int BB, int XM>
-__global__ void __launch_bounds__(1024) k_prod_f(ProdArgs a) {
+__global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB == 1 && Q >= 2) ? 8 : 1)
+    k_prod_f(ProdArgs a) {
   constexpr int RW = 64 / Q;
   constexpr int CW = Q * NWL;
   constexpr int G = CW * 8;           // 4-column groups per chunk (<= 64: one per lane)
@@ -153,10 +171,10 @@ __global__ void __launch_bounds__(1024) k_prod_f(ProdArgs a) {
   const int r = lane % RW;
   const int m = blockIdx.x * RW + r;
   const bool valid = m < a.M;
-  const int mload = valid ? m : a.M - 1;  // rows beyond M load a valid row; their sums are dropped
+  const SignRows<KM> srows = sign_rows<KM, RW>(a, m);  // rows beyond M read padding; their sums are dropped
+  const ActSrc asrc = act_src(a);
   const bool cs = a.colscale != nullptr;
   const int KX = cs ? a.K : 1;
-  const int ndfull = a.ND & ~3;           // words in complete 4-word layout tiles
   const uint32_t wbase_lds = (uint32_t)wv * a.wave_lds;
   const bool builder = lane < G;  // this lane builds the tables of group `lane`
 
@@ -166,18 +184,23 @@ __global__ void __launch_bounds__(1024) k_prod_f(ProdArgs a) {
 #pragma unroll
     for (int b = 0; b < BB; ++b) acc[k][b] = 0.0f;
 
-  // First chunk: sign words, then activations and column scales, all in flight at once.
+  // First chunk: activations and column scales, row scales, then sign words,
+  // all in flight at once.  Loads complete in issue order, so the table build
+  // (which needs only the activations) need not wait for the sign words.
   uint32_t cur[KM][NWL], nxt[KM][NWL];
   ActRaw<KM, BB> act;
+  float al[KM];
   {
     const int cw0 = wv * a.NCH * CW;
-    load_chunk<KM, NWL>(a, cw0 + CW <= ndfull, mload, cw0 + q * NWL, cur);
-    fetch_act<KM, BB, XM>(a, cs, cw0 * 32 + (builder ? lane : 0) * 4, act);
+    fetch_act<KM, BB, XM>(a, asrc, cw0 * 32 + (builder ? lane : 0) * 4, act);
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (base_active<KM>(a, k)) al[k] = __uint_as_float(ld32(asrc.al, (uint32_t)(k * a.M + m) * 4u));
+    load_chunk<KM, NWL>(a, srows, cw0 + q * NWL, cur);
   }
 
   for (int c = 0; c < a.NCH; ++c) {
     const int cw0 = (wv * a.NCH + c) * CW;  // first word of the chunk
-    if (c + 1 < a.NCH) load_chunk<KM, NWL>(a, cw0 + 2 * CW <= ndfull, mload, cw0 + CW + q * NWL, nxt);
 
     // ---- tables: the 16 signed sums of 4-column group `lane` of the chunk
     if (builder) {
@@ -191,8 +214,9 @@ __global__ void __launch_bounds__(1024) k_prod_f(ProdArgs a) {
             float xv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float d = XM == 1   ? bf16_bits_to_float((uint16_t)act.x[b][j])
-                              : XM == 2 ? f16_bits_to_float((uint16_t)act.x[b][j])
+              const uint32_t pk = act.x[0][j >> 1];  // XM != 0: two 16-bit values per word
+              const float d = XM == 1   ? __uint_as_float((j & 1) ? (pk & 0xffff0000u) : (pk << 16))
+                              : XM == 2 ? f16_bits_to_float((uint16_t)((j & 1) ? (pk >> 16) : pk))
                                         : decode_x(act.x[b][j], a.xdt);
               xv[j] = (inb && a.b0 + b < a.B) ? d : 0.0f;
             }
@@ -214,17 +238,19 @@ __global__ void __launch_bounds__(1024) k_prod_f(ProdArgs a) {
         }
       }
     }
-    if (c + 1 < a.NCH) fetch_act<KM, BB, XM>(a, cs, (cw0 + CW) * 32 + (builder ? lane : 0) * 4, act);
-    __syncthreads();
+    // next chunk: activations (their registers are free once the tables are
+    // built), then sign words; the next build waits only for the activations
+    if (c + 1 < a.NCH) {
+      fetch_act<KM, BB, XM>(a, asrc, (cw0 + CW) * 32 + (builder ? lane : 0) * 4, act);
+      load_chunk<KM, NWL>(a, srows, cw0 + CW + q * NWL, nxt);
+    }
+    wave_sync();  // the tables are private to this wavefront
 
     // ---- lookups: one table read and one add per 4 weights
-    if (cw0 + CW <= a.ND)
-      lookup_chunk<Q, NWL, KM, BB, true>(a, lds, wbase_lds, cs, q, cw0 + q * NWL, cur, acc);
-    else
-      lookup_chunk<Q, NWL, KM, BB, false>(a, lds, wbase_lds, cs, q, cw0 + q * NWL, cur, acc);
+    lookup_chunk<Q, NWL, KM, BB>(a, lds, wbase_lds, cs, q, cur, acc);
 
     if (c + 1 < a.NCH) {
-      __syncthreads();  // the next chunk's tables overwrite these
+      wave_sync();  // the next chunk's tables overwrite these
 #pragma unroll
       for (int k = 0; k < KM; ++k)
 #pragma unroll
@@ -240,9 +266,9 @@ __global__ void __launch_bounds__(1024) k_prod_f(ProdArgs a) {
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
       if (base_active<KM>(a, k)) {
-        const float al = row_alpha(a, k, m);
+        const float alk = a.alpha ? al[k] : 1.0f;
 #pragma unroll
-        for (int b = 0; b < BB; ++b) tot[b] += al * acc[k][b];
+        for (int b = 0; b < BB; ++b) tot[b] += alk * acc[k][b];
       }
     }
   }
@@ -261,8 +287,7 @@ __global__ void __launch_bounds__(1024) k_prod_f(ProdArgs a) {
     const int rr = t / BB, b = t % BB;
     const int mm = blockIdx.x * RW + rr;
     if (mm < a.M && a.b0 + b < a.B) {
-      float s = 0.0f;
-      for (int w = 0; w < a.W; ++w) s += red[(w * RW + rr) * BB + b];
+      const float s = sum_waves(red + rr * BB + b, RW * BB, a.W);
       const size_t yi = (size_t)mm * a.B + a.b0 + b;
       a.y[yi] = (a.accumulate ? a.y[yi] : 0.0f) + s;
     }
@@ -282,7 +307,7 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8) {
   ProdPlan p{};
   const int ND = N / 32;
   p.KM = K <= 4 ? K : 8;
-  p.BB = B <= 1 ? 1 : B <= 2 ? 2 : 4;
+  p.BB = (B <= 1 || (i8 && p.KM == 8)) ? 1 : (B <= 2 || p.KM == 8) ? 2 : 4;
   p.nlaunch = (B + p.BB - 1) / p.BB;
   // lanes per row: the fewest that still give at least 256 workgroups
   const int forceQ = env_int("BSG_Q", 0);
@@ -306,7 +331,8 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8) {
   p.wave_lds = i8 ? (size_t)p.CW * p.BB * 12 * 4 : (size_t)KX * p.BB * (p.NWL * 8) * (p.Q * 64 + 16);
   const int T = (ND + p.CW - 1) / p.CW;  // chunks
   int W = env_int("BSG_WAVES", 16);
-  W = W > 16 ? 16 : W;
+  const int wmax = prod_max_waves(p.KM, p.BB);
+  W = W > wmax ? wmax : W;
   W = W > T ? T : W;
   const size_t red_per_wave = (size_t)p.RW * p.BB * 4 * (i8 ? p.KM : 1);
   while (W > 1 && (size_t)W * (p.wave_lds + red_per_wave) > kMaxLds) --W;

@@ -17,7 +17,7 @@
 namespace bsg {
 
 template <int Q, int NWL, int KM, int BB, int XM>
-__global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
+__global__ void __launch_bounds__(64 * prod_max_waves(KM, BB)) k_prod_i8(ProdArgs a) {
   constexpr int RW = 64 / Q;
   constexpr int CW = Q * NWL;
   extern __shared__ __align__(16) char lds[];
@@ -28,8 +28,8 @@ __global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
   const int r = lane % RW;
   const int m = blockIdx.x * RW + r;
   const bool valid = m < a.M;
-  const int mload = valid ? m : a.M - 1;  // rows beyond M load a valid row; their sums are dropped
-  const int ndfull = a.ND & ~3;
+  const SignRows<KM> srows = sign_rows<KM, RW>(a, m);  // rows beyond M read padding; their sums are dropped
+  const rsrc_t xsrc = make_rsrc(a.xq, (size_t)a.N * a.B);
   uint32_t* pl = (uint32_t*)(lds + (size_t)wv * a.wave_lds);
 
   int cnt[KM][BB][8];
@@ -43,19 +43,44 @@ __global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
       for (int p = 0; p < 8; ++p) cnt[k][b][p] = 0;
   }
 
-  uint32_t cur[KM][NWL], nxt[KM][NWL];
-  load_chunk<KM, NWL>(a, wv * a.NCH * CW + CW <= ndfull, mload, wv * a.NCH * CW + q * NWL, cur);
-
-  for (int c = 0; c < a.NCH; ++c) {
-    const int cw0 = (wv * a.NCH + c) * CW;
-    if (c + 1 < a.NCH) load_chunk<KM, NWL>(a, cw0 + 2 * CW <= ndfull, mload, cw0 + CW + q * NWL, nxt);
-
-    // ---- bit planes: one ballot over 64 lanes covers two sign words
+  // activations of a chunk: column (cw0 + 2u) * 32 + lane for u < CW/2,
+  // unconditional loads (columns beyond N read 0; batch columns beyond B
+  // read column B-1 and are zeroed when used)
+  int xv[CW / 2][BB], xn[CW / 2][BB];
+  auto fetch_xq = [&](int cw0, int (&dst)[CW / 2][BB]) {
+#pragma unroll
     for (int u = 0; u < CW / 2; ++u) {
       const int n = (cw0 + 2 * u) * 32 + lane;
 #pragma unroll
       for (int b = 0; b < BB; ++b) {
-        const int v = (n < a.N && a.b0 + b < a.B) ? (int)a.xq[(size_t)n * a.B + a.b0 + b] : 0;
+        const int bb = a.b0 + b < a.B ? a.b0 + b : a.B - 1;
+        dst[u][b] = (int)(int8_t)ld8(xsrc, (uint32_t)(n * a.B + bb));  // 0 beyond N
+      }
+    }
+  };
+  auto keep_xq = [&](int cw0, int u, int b, int v) {
+    return ((cw0 + 2 * u) * 32 + lane < a.N && a.b0 + b < a.B) ? v : 0;
+  };
+
+  // activations first: loads complete in issue order, so the bit planes need
+  // not wait for the sign words
+  uint32_t cur[KM][NWL], nxt[KM][NWL];
+  fetch_xq(wv * a.NCH * CW, xv);
+  load_chunk<KM, NWL>(a, srows, wv * a.NCH * CW + q * NWL, cur);
+
+  for (int c = 0; c < a.NCH; ++c) {
+    const int cw0 = (wv * a.NCH + c) * CW;
+    if (c + 1 < a.NCH) {
+      fetch_xq(cw0 + CW, xn);
+      load_chunk<KM, NWL>(a, srows, cw0 + CW + q * NWL, nxt);
+    }
+
+    // ---- bit planes: one ballot over 64 lanes covers two sign words
+#pragma unroll
+    for (int u = 0; u < CW / 2; ++u) {
+#pragma unroll
+      for (int b = 0; b < BB; ++b) {
+        const int v = keep_xq(cw0, u, b, xv[u][b]);
         uint32_t lo[8], hi[8];
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
@@ -77,12 +102,13 @@ __global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
         }
       }
     }
-    __syncthreads();
+    wave_sync();  // the planes are private to this wavefront
 
-    const int lw0 = cw0 + q * NWL;
+    // words beyond ND are zero (padding, or out of range) and so are the
+    // planes of their columns: they add 0, no guard
 #pragma unroll
     for (int j = 0; j < NWL; ++j) {
-      if (lw0 + j < a.ND) {
+      {
 #pragma unroll
         for (int b = 0; b < BB; ++b) {
           const uint32_t* src = pl + ((size_t)(q * NWL + j) * BB + b) * 12;
@@ -95,17 +121,25 @@ __global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
             if (base_active<KM>(a, k)) {
 #pragma unroll
               for (int p = 0; p < 8; ++p) cnt[k][b][p] += __builtin_popcount(cur[k][j] & P[p]);
+              // finish this word's counts here (left free, the compiler sinks
+              // them to the end of the loop body and runs out of registers)
+#pragma unroll
+              for (int p = 0; p < 8; ++p) asm volatile("" : "+v"(cnt[k][b][p]));
             }
           }
         }
       }
     }
-    __syncthreads();
+    wave_sync();  // the next chunk's planes overwrite these
     if (c + 1 < a.NCH) {
 #pragma unroll
       for (int k = 0; k < KM; ++k)
 #pragma unroll
         for (int j = 0; j < NWL; ++j) cur[k][j] = nxt[k][j];
+#pragma unroll
+      for (int u = 0; u < CW / 2; ++u)
+#pragma unroll
+        for (int b = 0; b < BB; ++b) xv[u][b] = xn[u][b];
     }
   }
 
@@ -132,8 +166,7 @@ __global__ void __launch_bounds__(1024) k_prod_i8(ProdArgs a) {
     if (mm < a.M && a.b0 + b < a.B) {
       float ysum = 0.0f;
       for (int k = 0; k < a.K; ++k) {
-        int s = 0;
-        for (int w = 0; w < a.W; ++w) s += red[((w * RW + rr) * KM + k) * BB + b];
+        const int s = sum_waves(red + (rr * KM + k) * BB + b, RW * KM * BB, a.W);
         if (a.acc) a.acc[((size_t)k * a.M + mm) * a.B + a.b0 + b] = s;
         if (a.y) ysum += (a.alpha ? a.alpha[(size_t)k * a.M + mm] : 1.0f) * (float)s;
       }

@@ -17,21 +17,17 @@ constexpr int kMaxB = 64;
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
 // Words of one base in the device layout: M*ND rounded up to 64 words.
-__host__ __device__ inline size_t plane_words(int M, int ND) {
-  size_t w = (size_t)M * (size_t)ND;
-  return (w + 63) / 64 * 64;
-}
+// Device layout (documented in bsg.h): rows padded to a multiple of 64,
+// words per row to a multiple of 4, whole 64 x 4-word tiles.
+__host__ __device__ inline int pad_rows(int M) { return (M + 63) & ~63; }
+__host__ __device__ inline int pad_words(int ND) { return (ND + 3) & ~3; }
+__host__ __device__ inline size_t plane_words(int M, int ND) { return (size_t)pad_rows(M) * (size_t)pad_words(ND); }
 
-// Device-layout word offset of logical word w of row m of base k (the formula
-// documented in bsg.h).
+// Device-layout word offset of logical word w of row m of base k.
 __host__ __device__ inline size_t layout_offset(int M, int ND, size_t plane, int k, int m, int w) {
-  size_t rb = (size_t)m >> 6, r = (size_t)m & 63;
-  size_t h = (size_t)M - rb * 64;
-  if (h > 64) h = 64;
-  size_t g = (size_t)w >> 2, j = (size_t)w & 3;
-  size_t wg = (size_t)ND - g * 4;
-  if (wg > 4) wg = 4;
-  return (size_t)k * plane + rb * 64 * (size_t)ND + g * 4 * h + r * wg + j;
+  (void)M;
+  return (size_t)k * plane + (size_t)(m >> 6) * 64 * (size_t)pad_words(ND) + (size_t)(w >> 2) * 256 +
+         (size_t)(m & 63) * 4 + (size_t)(w & 3);
 }
 
 // bf16 / fp16 bit patterns -> fp32 (exact).
@@ -76,7 +72,6 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool int8_mode);
 struct ProdArgs {
   const uint32_t* bits;
   const float* alpha;        // fp32 [K][M], or NULL
-  const uint16_t* alpha_h;   // fp16 [K][M], or NULL (both NULL: 1)
   const uint16_t* colscale;  // fp16 [K][N], or NULL
   const void* x;             // [N][B] of dtype xdt (float path)
   const int8_t* xq;          // [N][B] (int8 path)

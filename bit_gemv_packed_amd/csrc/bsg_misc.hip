@@ -73,15 +73,18 @@ __global__ void __launch_bounds__(256) k_quantize(const void* __restrict__ x, in
   }
 }
 
+// Writes every word of the K padded planes: the logical word, or 0 in the padding.
 __global__ void k_to_layout(const uint32_t* __restrict__ logical, int K, int M, int ND, size_t plane,
                             uint32_t* __restrict__ bits) {
-  const size_t total = (size_t)K * M * ND;
+  const size_t total = (size_t)K * plane;
+  const size_t ndp = (size_t)pad_words(ND);
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const int w = (int)(i % ND);
-    const size_t km = i / ND;
-    const int m = (int)(km % M);
-    const int k = (int)(km / M);
-    bits[layout_offset(M, ND, plane, k, m, w)] = logical[i];
+    const int k = (int)(i / plane);
+    const size_t o = i % plane;
+    const size_t rb = o / (64 * ndp), t = o % (64 * ndp);  // row block, offset in it
+    const int m = (int)(rb * 64 + (t % 256) / 4);
+    const int w = (int)((t / 256) * 4 + t % 4);
+    bits[i] = (m < M && w < ND) ? logical[((size_t)k * M + m) * ND + w] : 0u;
   }
 }
 
@@ -119,7 +122,8 @@ hipError_t launch_layout(const uint32_t* src, int K, int M, int N, uint32_t* dst
   const size_t plane = plane_words(M, ND);
   const size_t total = (size_t)K * M * ND;
   if (to_layout)
-    hipLaunchKernelGGL(k_to_layout, dim3(grid_for(total, 256)), dim3(256), 0, st, src, K, M, ND, plane, dst);
+    hipLaunchKernelGGL(k_to_layout, dim3(grid_for((size_t)K * plane, 256)), dim3(256), 0, st, src, K, M, ND, plane,
+                       dst);
   else
     hipLaunchKernelGGL(k_from_layout, dim3(grid_for(total, 256)), dim3(256), 0, st, src, K, M, ND, plane, dst);
   return hipGetLastError();

@@ -62,16 +62,18 @@ __global__ void __launch_bounds__(kT) k_rowsum(const double* __restrict__ R, con
 template <typename T>
 __global__ void __launch_bounds__(64) k_signs(const T* __restrict__ R, int M, int N, uint32_t* __restrict__ bits,
                                              size_t plane, int k) {
+  // one workgroup per padded row: every word of the row, padding included
   const int m = blockIdx.x;
   const int ND = N / 32;
-  for (int n0 = 0; n0 < N; n0 += 64) {
+  const int NP = pad_words(ND) * 32;
+  for (int n0 = 0; n0 < NP; n0 += 64) {
     const int n = n0 + threadIdx.x;
-    const bool pos = n < N && R[(size_t)m * N + n] >= (T)0;
+    const bool pos = m < M && n < N && R[(size_t)m * N + n] >= (T)0;
     const unsigned long long b = __ballot(pos);
     if (threadIdx.x == 0) {
-      const int w = n0 / 32;
+      const int w = n0 / 32;  // even; w + 1 < NP / 32
       bits[layout_offset(M, ND, plane, k, m, w)] = (uint32_t)b;
-      if (w + 1 < ND) bits[layout_offset(M, ND, plane, k, m, w + 1)] = (uint32_t)(b >> 32);
+      bits[layout_offset(M, ND, plane, k, m, w + 1)] = (uint32_t)(b >> 32);
     }
   }
 }
@@ -226,7 +228,7 @@ hipError_t launch_pack(const float* W, int M, int N, int K, bool colscale, uint3
   for (int k = 0; k < K; ++k) {
     float* ak = alpha + (size_t)k * M;
     uint16_t* ck = colscale ? cs + (size_t)k * N : nullptr;
-    hipLaunchKernelGGL(k_signs<double>, dim3(M), dim3(64), 0, st, R, M, N, bits, plane, k);
+    hipLaunchKernelGGL(k_signs<double>, dim3(pad_rows(M)), dim3(64), 0, st, R, M, N, bits, plane, k);
     hipLaunchKernelGGL(k_rowsum<0>, dim3((M + kT - 1) / kT), dim3(kT), 0, st, R, (const float*)nullptr,
                        (const float*)nullptr, M, N, ak, (double*)nullptr);
     if (colscale) {
@@ -241,7 +243,7 @@ hipError_t launch_pack(const float* W, int M, int N, int K, bool colscale, uint3
 }
 
 hipError_t launch_pack_signs(const float* S, int M, int N, uint32_t* bits, hipStream_t st) {
-  hipLaunchKernelGGL(k_signs<float>, dim3(M), dim3(64), 0, st, S, M, N, bits, plane_words(M, N / 32), 0);
+  hipLaunchKernelGGL(k_signs<float>, dim3(pad_rows(M)), dim3(64), 0, st, S, M, N, bits, plane_words(M, N / 32), 0);
   return hipGetLastError();
 }
 

@@ -33,73 +33,108 @@ __device__ inline bool base_active(const ProdArgs& a, int k) {
   return KM <= 4 || k < a.K;
 }
 
+// Buffer resources.  Operands are read with buffer loads: a 128-bit
+// descriptor in scalar registers (base, size in bytes) plus a 32-bit byte
+// offset per lane.  That halves the address registers of 64-bit pointers,
+// and a read at or beyond the size returns 0 without touching memory (a
+// descriptor of size 0 for an absent operand reads all zeros).  Word 3 of
+// the descriptor is the gfx9 raw-buffer setting (32-bit data format).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* p, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+__device__ inline uint32_t ld32(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+__device__ inline uint2 ld64(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+__device__ inline uint4 ld128(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ inline uint32_t ld16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
+__device__ inline uint32_t ld8(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0); }
+
+// The sign words of one workgroup: all its rows lie in one 64-row block
+// (RW divides 64), so each base's block is one resource, uniform over the
+// workgroup: 64 rows x NDP words (padded layout, bsg.h).  Row blocks hold
+// zero words in their padding rows and words, so rows beyond M and words
+// beyond ND need no guard; words beyond NDP are out of range and read 0.
+template <int KM>
+struct SignRows {
+  rsrc_t r[KM];
+  uint32_t row_off;  // byte offset of this lane's row in a tile: (m % 64) * 16
+};
+template <int KM, int RW>
+__device__ inline SignRows<KM> sign_rows(const ProdArgs& a, int m) {
+  SignRows<KM> s;
+  const int rb = (int)(blockIdx.x * RW) >> 6;
+  const size_t blk = (size_t)64 * pad_words(a.ND);  // words of one row block
+  s.row_off = (uint32_t)(m & 63) * 16u;
+#pragma unroll
+  for (int k = 0; k < KM; ++k)
+    s.r[k] = make_rsrc(a.bits + (size_t)(k < a.K ? k : 0) * a.plane + (size_t)rb * blk, blk * 4);
+  return s;
+}
+
 // Sign words of one chunk: NWL consecutive logical words [w0, w0 + NWL) of
-// row m for every base k < K (w0 is a multiple of min(NWL, 4)).
-//
-// load_chunk_full: every word of the chunk lies in a complete 4-word layout
-// tile (the caller checks this once per wavefront); straight-line 4/8/16-byte
-// loads, all in flight together.  m must be a valid row (callers clamp rows
-// beyond M to M-1 and discard their sums).
+// the lane's row for every base k < K (w0 is a multiple of min(NWL, 4)):
+// 4-, 8- or 16-byte loads at tile (w0 / 4) * 1 KiB + row * 16 + (w0 % 4) * 4.
 template <int KM, int NWL>
-__device__ inline void load_chunk_full(const ProdArgs& a, int m, int w0, uint32_t (&wd)[KM][NWL]) {
-  const int rb = m >> 6, rt = m & 63;
-  const int h = min(64, a.M - rb * 64);
+__device__ inline void load_chunk(const ProdArgs& a, const SignRows<KM>& s, int w0, uint32_t (&wd)[KM][NWL]) {
   constexpr int PW = NWL < 4 ? NWL : 4;  // words per load
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
     if (base_active<KM>(a, k)) {
-      const uint32_t* base = a.bits + (size_t)k * a.plane + (size_t)rb * 64 * a.ND;
 #pragma unroll
       for (int g = 0; g < NWL / PW; ++g) {
         const int wf = w0 + g * PW;
-        const uint32_t* p = base + (size_t)(wf >> 2) * 4 * h + rt * 4 + (wf & 3);
+        const uint32_t off = (uint32_t)(wf >> 2) * 1024u + s.row_off + (uint32_t)(wf & 3) * 4u;
         if (PW == 4) {
-          const uint4 v = *(const uint4*)p;
+          const uint4 v = ld128(s.r[k], off);
           wd[k][g * 4 + 0] = v.x;
           wd[k][g * 4 + 1] = v.y;
           wd[k][g * 4 + 2] = v.z;
           wd[k][g * 4 + 3] = v.w;
         } else if (PW == 2) {
-          const uint2 v = *(const uint2*)p;
+          const uint2 v = ld64(s.r[k], off);
           wd[k][g * 2 + 0] = v.x;
           wd[k][g * 2 + 1] = v.y;
         } else {
-          wd[k][g] = p[0];
+          wd[k][g] = ld32(s.r[k], off);
         }
       }
     }
   }
 }
 
-// load_chunk_any: the last, ragged chunk; one guarded load per word, words at
-// or beyond ND read as 0 (their lookups are skipped).
-template <int KM, int NWL>
-__device__ inline void load_chunk_any(const ProdArgs& a, int m, int w0, uint32_t (&wd)[KM][NWL]) {
-  const int rb = m >> 6, rt = m & 63;
-  const int h = min(64, a.M - rb * 64);
-#pragma unroll
-  for (int k = 0; k < KM; ++k) {
-    if (base_active<KM>(a, k)) {
-      const uint32_t* base = a.bits + (size_t)k * a.plane + (size_t)rb * 64 * a.ND;
-#pragma unroll
-      for (int j = 0; j < NWL; ++j) {
-        const int w = w0 + j;
-        const int g4 = w >> 2;
-        const int wg = min(4, a.ND - 4 * g4);
-        wd[k][j] = w < a.ND ? base[(size_t)g4 * 4 * h + rt * wg + (w & 3)] : 0u;
-      }
-    }
-  }
+// Orders this wavefront's LDS writes before its later LDS reads (and reads
+// before later writes) across its lanes; no workgroup barrier.
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Loads the sign words of chunk [cw0, cw0 + CW) for this lane (quarter q);
-// `full` must be uniform across the wavefront.
-template <int KM, int NWL>
-__device__ inline void load_chunk(const ProdArgs& a, bool full, int m, int w0, uint32_t (&wd)[KM][NWL]) {
-  if (full)
-    load_chunk_full<KM, NWL>(a, m, w0, wd);
-  else
-    load_chunk_any<KM, NWL>(a, m, w0, wd);
+// Most wavefronts per workgroup of an instance: 16, or 8 where KM * BB >= 8
+// partial sums (and as many sign-word sets) live in registers, so that the
+// kernel has up to 256 VGPRs and does not spill.
+constexpr int prod_max_waves(int KM, int BB) { return KM * BB >= 8 ? 8 : 16; }
+
+// Sum of the W <= 16 per-wavefront partials p[0], p[stride], ... read from
+// LDS all at once (straight-line), added in a fixed order.
+template <typename T>
+__device__ inline T sum_waves(const T* p, int stride, int W) {
+  T v[16];
+#pragma unroll
+  for (int w = 0; w < 16; ++w) v[w] = p[(w < W ? w : W - 1) * stride];  // in-bounds read, then mask
+#pragma unroll
+  for (int w = 0; w < 16; ++w) v[w] = w < W ? v[w] : T(0);
+#pragma unroll
+  for (int h = 8; h >= 1; h >>= 1)
+#pragma unroll
+    for (int w = 0; w < h; ++w) v[w] += v[w + h];
+  return v[0];
 }
 
 template <typename Kern>
@@ -124,11 +159,18 @@ inline hipError_t launch_one(Kern kern, const ProdPlan& p, const ProdArgs& a, hi
   BSG_PROD_XM(X, 1, 8, 1) BSG_PROD_XM(X, 1, 8, 2) BSG_PROD_XM(X, 4, 1, 3) BSG_PROD_XM(X, 4, 1, 4)            \
   BSG_PROD_XM(X, 4, 1, 8) BSG_PROD_XM(X, 2, 2, 3) BSG_PROD_XM(X, 2, 2, 4) BSG_PROD_XM(X, 2, 2, 8)            \
   BSG_PROD_XM(X, 1, 4, 3) BSG_PROD_XM(X, 1, 4, 4) BSG_PROD_XM(X, 1, 4, 8) BSG_PROD_MULTI_B(X, 2)             \
-  BSG_PROD_MULTI_B(X, 4)
+  BSG_PROD_I8_MULTI_B(X, 4)
 #define BSG_PROD_I8_INSTANCES(X)                                                                       \
   X(4, 2, 1, 1, 0) X(4, 2, 2, 1, 0) X(2, 4, 1, 1, 0) X(2, 4, 2, 1, 0) X(1, 8, 1, 1, 0) X(1, 8, 2, 1, 0) \
   X(4, 1, 3, 1, 0) X(4, 1, 4, 1, 0) X(4, 1, 8, 1, 0) X(2, 2, 3, 1, 0) X(2, 2, 4, 1, 0) X(2, 2, 8, 1, 0) \
-  X(1, 4, 3, 1, 0) X(1, 4, 4, 1, 0) X(1, 4, 8, 1, 0) BSG_PROD_MULTI_B(X, 2) BSG_PROD_MULTI_B(X, 4)
+  X(1, 4, 3, 1, 0) X(1, 4, 4, 1, 0) X(1, 4, 8, 1, 0) BSG_PROD_I8_MULTI_B(X, 2) BSG_PROD_I8_MULTI_B(X, 4)
+// Several batch columns with K <= 4 (float: K > 4 takes at most two batch
+// columns per launch; int8: one, as 8 plane counters per base and column
+// would not fit in registers)
+#define BSG_PROD_I8_MULTI_B(X, BB)                                                                     \
+  X(4, 1, 1, BB, 0) X(4, 1, 2, BB, 0) X(4, 1, 3, BB, 0) X(4, 1, 4, BB, 0)                              \
+  X(2, 2, 1, BB, 0) X(2, 2, 2, BB, 0) X(2, 2, 3, BB, 0) X(2, 2, 4, BB, 0)                              \
+  X(1, 4, 1, BB, 0) X(1, 4, 2, BB, 0) X(1, 4, 3, BB, 0) X(1, 4, 4, BB, 0)
 #define BSG_PROD_MULTI_B(X, BB)                                                                        \
   X(4, 1, 1, BB, 0) X(4, 1, 2, BB, 0) X(4, 1, 3, BB, 0) X(4, 1, 4, BB, 0) X(4, 1, 8, BB, 0)            \
   X(2, 2, 1, BB, 0) X(2, 2, 2, BB, 0) X(2, 2, 3, BB, 0) X(2, 2, 4, BB, 0) X(2, 2, 8, BB, 0)            \

@@ -44,14 +44,14 @@
  *
  * Device sign layout (what every kernel reads), for K bases of an M x N
  * matrix with ND = N/32 words per row:
- *   plane  = round_up(M*ND, 64)                     words per base
- *   rb = m / 64, r = m % 64, h = min(64, M - 64*rb) rows in row block rb
- *   g  = w / 4,  j = w % 4,  wg = min(4, ND - 4*g)  words in word group g
- *   offset(k, m, w) = k*plane + rb*64*ND + g*4*h + r*wg + j
- * i.e. tiles of 64 rows x 4 words (128 columns), each stored row-major, one
- * after the other along the words of a 64-row block; the last row block and
- * the last word group may be narrower.  A full tile is one contiguous KiB,
- * which a 64-lane wavefront reads with one 16-byte load per lane.
+ *   MP = round_up(M, 64), NDP = round_up(ND, 4)     padded rows, words per row
+ *   plane = MP*NDP                                  words per base
+ *   offset(k, m, w) = k*plane + (m/64)*64*NDP + (w/4)*256 + (m%64)*4 + w%4
+ * i.e. tiles of 64 rows x 4 words (128 columns), each one contiguous KiB
+ * stored row-major, one after the other along the words of a 64-row block,
+ * then the next row block.  Rows M..MP-1 and words ND..NDP-1 are padding and
+ * hold zero words (every writer of this layout writes them).  A wavefront
+ * reads a tile with one 16-byte load per lane.
  */
 #ifndef BSG_H
 #define BSG_H

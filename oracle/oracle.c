@@ -402,28 +402,25 @@ OR_API int or_salient_select(const float* W, int M, int N, const float* xbar, in
 /* ------------------------------------------------------------------ */
 
 /*
- * The device layout groups the sign words of each base into tiles of 64 rows
- * by 4 words (128 columns); a tile is stored row-major; tiles follow each
- * other along the words of a 64-row block, then along the row blocks; the
- * last row block and the last word group may be narrower.  Each base starts
- * at a multiple of 64 words.
+ * The device layout pads the rows of each base to a multiple of 64 and the
+ * words of each row to a multiple of 4 (zero words), and stores the result
+ * as tiles of 64 rows by 4 words (128 columns): a tile is 256 consecutive
+ * words in row-major order; tiles follow each other along the words of a
+ * 64-row block, then along the row blocks; the bases follow each other.
  */
+static size_t or_round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
 OR_API size_t or_layout_plane_words(int M, int N) {
   size_t nd = (size_t)(N + 31) / 32;
-  size_t w = (size_t)M * nd;
-  return (w + 63) / 64 * 64;
+  return or_round_up((size_t)M, 64) * or_round_up(nd, 4);
 }
 
 OR_API size_t or_layout_offset(int K, int M, int N, int k, int m, int w) {
   (void)K;
-  size_t nd = (size_t)(N + 31) / 32;
-  size_t rb = (size_t)m / 64, r = (size_t)m % 64;
-  size_t h = (size_t)M - rb * 64;
-  if (h > 64) h = 64;
-  size_t g = (size_t)w / 4, j = (size_t)w % 4;
-  size_t wg = nd - g * 4;
-  if (wg > 4) wg = 4;
-  return (size_t)k * or_layout_plane_words(M, N) + rb * 64 * nd + g * 4 * h + r * wg + j;
+  size_t ndp = or_round_up((size_t)(N + 31) / 32, 4);
+  size_t block = (size_t)m / 64, row = (size_t)m % 64; /* row block, row in it */
+  size_t tile = (size_t)w / 4, col = (size_t)w % 4;    /* tile along the row, word in it */
+  return (size_t)k * or_layout_plane_words(M, N) + block * 64 * ndp + tile * 256 + row * 4 + col;
 }
 
 OR_API void or_logical_to_layout(const uint32_t* logical, int K, int M, int N, uint32_t* phys) {

@@ -376,27 +376,38 @@ def test_absmean():
 
 # ----------------------------------------------------------- layout
 @pytest.mark.parametrize("K,M,N", [(1, 64, 128), (2, 70, 160), (3, 130, 32), (1, 1, 96), (2, 200, 544)])
-def test_layout_is_a_bijection_and_tiles_are_row_major(K, M, N):
+def test_layout_is_a_bijection_of_padded_tiles(K, M, N):
     nd = oracle.words(N)
+    mp, ndp = -(-M // 64) * 64, -(-nd // 4) * 4
     total = oracle.layout_words(K, M, N)
     plane = total // K
-    assert plane % 64 == 0 and plane >= M * nd
+    assert plane == mp * ndp and total == K * plane
     seen = set()
     for k in range(K):
         for m in range(M):
             for w in range(nd):
                 o = oracle.layout_offset(K, M, N, k, m, w)
-                assert k * plane <= o < k * plane + M * nd
+                assert k * plane <= o < (k + 1) * plane
                 seen.add(o)
     assert len(seen) == K * M * nd
-    # a full tile (64 rows x 4 words) is one contiguous row-major block of 256 words
-    if M >= 64 and nd >= 4:
-        base = oracle.layout_offset(K, M, N, 0, 0, 0)
-        for m in range(64):
-            for w in range(4):
-                assert oracle.layout_offset(K, M, N, 0, m, w) == base + m * 4 + w
+    # every tile (64 rows x 4 words) is one contiguous row-major block of 256 words
+    for k in range(K):
+        for rb in range(mp // 64):
+            for g in range(ndp // 4):
+                m0, w0 = rb * 64, g * 4
+                if m0 < M and w0 < nd:
+                    base = oracle.layout_offset(K, M, N, k, m0, w0)
+                    assert base % 256 == 0
+                    for m in range(m0, min(M, m0 + 64)):
+                        for w in range(w0, min(nd, w0 + 4)):
+                            assert oracle.layout_offset(K, M, N, k, m, w) == base + (m - m0) * 4 + (w - w0)
     L = synth.random_bits(K * M + N, K, M, N)
-    np.testing.assert_array_equal(oracle.from_layout(oracle.to_layout(L, K, M, N), K, M, N), L)
+    phys = oracle.to_layout(L, K, M, N)
+    assert phys.size == total
+    pad = np.ones(total, bool)
+    pad[sorted(seen)] = False
+    assert not phys[pad].any()  # padding rows and words are zero words
+    np.testing.assert_array_equal(oracle.from_layout(phys, K, M, N), L)
 
 
 # ----------------------------------------------------------- storage arithmetic
