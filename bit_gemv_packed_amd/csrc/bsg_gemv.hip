@@ -309,10 +309,17 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8) {
   p.KM = K <= 4 ? K : 8;
   p.BB = (B <= 1 || (i8 && p.KM == 8)) ? 1 : (B <= 2 || p.KM == 8) ? 2 : 4;
   p.nlaunch = (B + p.BB - 1) / p.BB;
-  // lanes per row: the fewest that still give at least 256 workgroups
+  // Lanes per row: the fewest that still give at least 256 workgroups
+  // (one per compute unit) -- except for very tall matrices (>= 256 row
+  // blocks of 64), which run 2 lanes per row in 8-wavefront workgroups: four
+  // such workgroups fit a compute unit's LDS, so every workgroup is resident
+  // at once (measured fastest on 28672 x 8192).
   const int forceQ = env_int("BSG_Q", 0);
+  const bool tall = M >= 64 * 256;
   if (forceQ == 1 || forceQ == 2 || forceQ == 4) {
     p.Q = forceQ;
+  } else if (tall) {
+    p.Q = 2;
   } else {
     p.Q = 4;
     for (int qq = 1; qq <= 4; qq *= 2) {
@@ -330,7 +337,7 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8) {
   p.NWL = p.CW / p.Q;
   p.wave_lds = i8 ? (size_t)p.CW * p.BB * 12 * 4 : (size_t)KX * p.BB * (p.NWL * 8) * (p.Q * 64 + 16);
   const int T = (ND + p.CW - 1) / p.CW;  // chunks
-  int W = env_int("BSG_WAVES", 16);
+  int W = env_int("BSG_WAVES", tall ? 8 : 16);
   const int wmax = prod_max_waves(p.KM, p.BB);
   W = W > wmax ? wmax : W;
   W = W > T ? T : W;
