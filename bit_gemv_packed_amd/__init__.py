@@ -54,6 +54,9 @@ _SIGS = {
     "bs_gemv_i8": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _I, _P]),
     "binlr_apply": (ctypes.c_int32, [_P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P, _SZ, _P]),
     "salient_int8_apply": (ctypes.c_int32, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _P]),
+    "bsg_linear_workspace_bytes": (_SZ, [_I, _I]),
+    "bsg_linear": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _I, _I, _P, _I,
+                                    _P, _SZ, _P]),
 }
 
 
@@ -288,6 +291,30 @@ def binlr_apply(U_bits, V_bits, alpha_r, r: int, M: int, N: int, x, y, workspace
     wp, wn = _ws_args(ws)
     _check("binlr_apply", lib().binlr_apply(_ptr(U_bits), _ptr(V_bits), _ptr(alpha_r), r, M, N, _ptr(x),
                                             _dtype_code(x), B, _ptr(y), wp, wn, _stream(dev)))
+    return y
+
+
+def bsg_linear(bits, K: int, M: int, N: int, alpha, x, colscale=None, lowrank=None, salient=None, y=None,
+               accumulate: bool = False, workspace=None):
+    """The whole layer in one pass over x: y (=/+=) bs_gemv term + binary low-rank correction + protected
+    int8 rows.  lowrank = (U_bits, V_bits, alpha_r, r) or None; salient = (rows, q, s) or None (rows
+    ascending)."""
+    torch = _torch()
+    B = _xshape(x, N)
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, B), dtype=torch.float32, device=dev)
+    U, V, ar, r = lowrank if lowrank is not None else (None, None, None, 0)
+    rows, q, sv = salient if salient is not None else (None, None, None)
+    ns = rows.numel() if rows is not None else 0
+    if ns == 0:
+        rows = q = sv = None
+    nb = int(lib().bsg_linear_workspace_bytes(r, B))
+    ws = workspace if workspace is not None else (_WS.get(nb, dev) if nb else None)
+    wp, wn = _ws_args(ws)
+    _check("bsg_linear", lib().bsg_linear(_ptr(bits), K, M, N, _ptr(alpha), _ptr(colscale), _ptr(U), _ptr(V),
+                                          _ptr(ar), r, _ptr(rows), ns, _ptr(q), _ptr(sv), _ptr(x), _dtype_code(x),
+                                          B, _ptr(y), 1 if accumulate else 0, wp, wn, _stream(dev)))
     return y
 
 

@@ -258,6 +258,79 @@ bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uin
   return hip_status(launch_prod_f(u, plan_prod(1, M, r, B, true, false), st));
 }
 
+size_t bsg_linear_workspace_bytes(int r, int B) {
+  if (r < 0 || (r % 32) != 0 || B < 1 || B > kMaxB) return 0;
+  return r > 0 ? binlr_ws(r, B) : 0;
+}
+
+bsg_status bsg_linear(const uint32_t* bits, int K, int M, int N, const float* alpha, const uint16_t* colscale,
+                      const uint32_t* U_bits, const uint32_t* V_bits, const uint16_t* alpha_r, int r,
+                      const int32_t* rows, int ns, const int8_t* q, const uint16_t* s_f16, const void* x,
+                      int x_dtype, int B, float* y, int accumulate, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
+  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || B < 1 || B > kMaxB || r < 0 || (r % 32) != 0 || ns < 0 ||
+      ns > M)
+    return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!bits || !alpha || !x || !y) return BSG_ERR_NULL;
+  if (r > 0 && (!U_bits || !V_bits || !alpha_r)) return BSG_ERR_NULL;
+  if (ns > 0 && (!rows || !q || !s_f16)) return BSG_ERR_NULL;
+  if (misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(colscale, 2) ||
+      misaligned(x, dtype_size(x_dtype)) || misaligned(y, 4) || misaligned(U_bits, 16) || misaligned(V_bits, 16) ||
+      misaligned(alpha_r, 2) || misaligned(rows, 4) || misaligned(q, 16) || misaligned(s_f16, 2) ||
+      misaligned(workspace, 16))
+    return BSG_ERR_ALIGN;
+  if (r > 0 && (!workspace || workspace_bytes < binlr_ws(r, B))) return BSG_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  float* z = (float*)workspace;
+
+  if (r > 0) {  // z' = V x (unit row scales; alpha_r is applied in the expansion)
+    ProdArgs v{};
+    v.bits = V_bits;
+    v.x = x;
+    v.y = z;
+    v.plane = plane_words(r, N / 32);
+    v.K = 1;
+    v.M = r;
+    v.N = N;
+    v.ND = N / 32;
+    v.B = B;
+    v.xdt = x_dtype;
+    v.xvec = xvec_ok(x, nullptr);
+    if (launch_prod_f(v, plan_prod(1, r, N, B, false, false), st) != hipSuccess) return BSG_ERR_HIP;
+  }
+  ProdArgs a{};
+  a.bits = bits;
+  a.alpha = alpha;
+  a.colscale = colscale;
+  a.x = x;
+  a.y = y;
+  a.plane = plane_words(M, N / 32);
+  a.K = K;
+  a.M = M;
+  a.N = N;
+  a.ND = N / 32;
+  a.B = B;
+  a.xdt = x_dtype;
+  a.accumulate = accumulate ? 1 : 0;
+  a.xvec = xvec_ok(x, colscale);
+  if (r > 0) {
+    a.lr_bits = U_bits;
+    a.lr_plane = plane_words(M, r / 32);
+    a.lr_z = z;
+    a.lr_scale = alpha_r;
+    a.lr_r = r;
+  }
+  if (ns > 0) {
+    a.sal_n = ns;
+    a.sal_rows = rows;
+    a.sal_q = q;
+    a.sal_s = s_f16;
+  }
+  return hip_status(launch_prod_f(a, plan_prod(K, M, N, B, colscale != nullptr, false), st));
+}
+
 bsg_status salient_int8_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s_f16, int M, int N,
                               const void* x, int x_dtype, int B, float* y, void* stream) {
   if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;

@@ -38,16 +38,36 @@ namespace bsg {
 typedef __attribute__((address_space(3))) const float lds_cf32;
 __device__ inline float lds_f32(uint32_t addr) { return *(lds_cf32*)(uintptr_t)addr; }
 
-// Resources of the activations, column scales and row scales (size 0 when
-// absent: their loads then read 0).
+// The activations one sign product multiplies: resources of x [N][B] and
+// of the column scales (size 0 when absent: their loads then read 0), and
+// the shape.  The main operand is x with the bases' column scales; the fused
+// low-rank expansion multiplies z = V x (fp32 [r][B]) with alpha_r as its
+// column scales.
 struct ActSrc {
-  rsrc_t x, c, al;
+  rsrc_t x, c;
+  int N, B, b0, xdt;
+  bool cs;
 };
 __device__ inline ActSrc act_src(const ProdArgs& a) {
   ActSrc s;
   s.x = make_rsrc(a.x, (size_t)a.N * a.B * (a.xdt == BSG_F32 ? 4 : 2));
   s.c = make_rsrc(a.colscale, a.colscale ? (size_t)a.K * a.N * 2 : 0);
-  s.al = make_rsrc(a.alpha, a.alpha ? (size_t)a.K * a.M * 4 : 0);
+  s.N = a.N;
+  s.B = a.B;
+  s.b0 = a.b0;
+  s.xdt = a.xdt;
+  s.cs = a.colscale != nullptr;
+  return s;
+}
+__device__ inline ActSrc lr_src(const ProdArgs& a) {
+  ActSrc s;
+  s.x = make_rsrc(a.lr_z, (size_t)a.lr_r * a.B * 4);
+  s.c = make_rsrc(a.lr_scale, (size_t)a.lr_r * 2);
+  s.N = a.lr_r;
+  s.B = a.B;
+  s.b0 = a.b0;
+  s.xdt = BSG_F32;
+  s.cs = true;
   return s;
 }
 
@@ -80,15 +100,15 @@ __device__ inline void fetch_act(const ProdArgs& a, const ActSrc& src, int n0, A
     r.x[0][1] = v.y;
 #pragma unroll
     for (int k = 0; k < KM; ++k)
-      if (base_active<KM>(a, k)) r.c[k] = ld64(src.c, (uint32_t)(k * a.N + n0) * 2u);
+      if (base_active<KM>(a, k)) r.c[k] = ld64(src.c, (uint32_t)(k * src.N + n0) * 2u);
   } else {
-    const uint32_t esz = a.xdt == BSG_F32 ? 4u : 2u;
+    const uint32_t esz = src.xdt == BSG_F32 ? 4u : 2u;
 #pragma unroll
     for (int b = 0; b < BB; ++b) {
-      const int bb = a.b0 + b < a.B ? a.b0 + b : a.B - 1;
+      const int bb = src.b0 + b < src.B ? src.b0 + b : src.B - 1;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t off = (uint32_t)((n0 + j) * a.B + bb) * esz;
+        const uint32_t off = (uint32_t)((n0 + j) * src.B + bb) * esz;
         const uint32_t lo = ld16(src.x, off), hi = ld16(src.x, off + 2);
         r.x[b][j] = esz == 4 ? (lo | (hi << 16)) : lo;
       }
@@ -96,9 +116,55 @@ __device__ inline void fetch_act(const ProdArgs& a, const ActSrc& src, int n0, A
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
       if (base_active<KM>(a, k)) {
-        const uint32_t off = (uint32_t)(k * a.N + n0) * 2u;
+        const uint32_t off = (uint32_t)(k * src.N + n0) * 2u;
         r.c[k] = make_uint2(ld16(src.c, off) | (ld16(src.c, off + 2) << 16),
                             ld16(src.c, off + 4) | (ld16(src.c, off + 6) << 16));
+      }
+    }
+  }
+}
+
+// Tables of one chunk: the 16 signed sums of 4-column group `lane` (columns
+// n_lane .. n_lane + 3), for each of the KX column-scale sets and each batch
+// column: entry e = sum_j (2 bit_j(e) - 1) c_j x_j (FluxBin Sec. 3.2: the
+// column scale is folded in while the table is built).  Columns at or beyond
+// N give a zero table.
+template <int Q, int NWL, int KM, int BB, int XM>
+__device__ inline void build_tables(const ActSrc& s, const ActRaw<KM, BB>& act, int KX, int lane, int n_lane,
+                                    char* lds, uint32_t wbase_lds) {
+  constexpr int STEPS = NWL * 8;          // groups per lane quarter
+  constexpr uint32_t ROWB = Q * 64 + 16;  // bytes of one step row: Q tables + 16 pad bytes
+  constexpr uint32_t REG = STEPS * ROWB;  // bytes of one (base, batch column) table set
+  const int qq = lane / STEPS, ii = lane % STEPS;
+  const bool inb = n_lane < s.N;
+#pragma unroll
+  for (int kx = 0; kx < KM; ++kx) {
+    if (kx < KX) {
+#pragma unroll
+      for (int b = 0; b < BB; ++b) {
+        float xv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t pk = act.x[0][j >> 1];  // XM != 0: two 16-bit values per word
+          const float d = XM == 1   ? __uint_as_float((j & 1) ? (pk & 0xffff0000u) : (pk << 16))
+                          : XM == 2 ? f16_bits_to_float((uint16_t)((j & 1) ? (pk >> 16) : pk))
+                                    : decode_x(act.x[b][j], s.xdt);
+          xv[j] = (inb && s.b0 + b < s.B) ? d : 0.0f;
+        }
+        if (s.cs) {
+          xv[0] *= f16_bits_to_float((uint16_t)(act.c[kx].x & 0xffffu));
+          xv[1] *= f16_bits_to_float((uint16_t)(act.c[kx].x >> 16));
+          xv[2] *= f16_bits_to_float((uint16_t)(act.c[kx].y & 0xffffu));
+          xv[3] *= f16_bits_to_float((uint16_t)(act.c[kx].y >> 16));
+        }
+        // bits 0,1 of e select the first pair's signed sum, bits 2,3 the second's
+        const float p0 = xv[0] + xv[1], m0 = xv[0] - xv[1];
+        const float p1 = xv[2] + xv[3], m1 = xv[2] - xv[3];
+        const float hi[4] = {-p1, m1, -m1, p1};
+        float4* dst =
+            (float4*)(lds + wbase_lds + (uint32_t)(kx * BB + b) * REG + (uint32_t)ii * ROWB + (uint32_t)qq * 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = make_float4(-p0 + hi[e], m0 + hi[e], -m0 + hi[e], p0 + hi[e]);
       }
     }
   }
@@ -119,34 +185,50 @@ __device__ inline void lookup_chunk(const ProdArgs& a, const char* lds, uint32_t
           (uint32_t)(uintptr_t)(lds + wbase_lds + (uint32_t)(cs ? k : 0) * BB * REG + (uint32_t)q * 64);
 #pragma unroll
       for (int j = 0; j < NWL; ++j) {
-        {
-          const uint32_t word = cur[k][j];
-          const uint32_t rl = __builtin_amdgcn_alignbit(word, word, 30) & 0x3c3c3c3cu;  // even slices * 4
-          const uint32_t rr = __builtin_amdgcn_alignbit(word, word, 2) & 0x3c3c3c3cu;   // odd slices * 4
-          uint32_t ad[8];
-          ad[0] = byte_add<0>(lbase, rl);
-          ad[1] = byte_add<0>(lbase, rr);
-          ad[2] = byte_add<1>(lbase, rl);
-          ad[3] = byte_add<1>(lbase, rr);
-          ad[4] = byte_add<2>(lbase, rl);
-          ad[5] = byte_add<2>(lbase, rr);
-          ad[6] = byte_add<3>(lbase, rl);
-          ad[7] = byte_add<3>(lbase, rr);
+        const uint32_t word = cur[k][j];
+        const uint32_t rl = __builtin_amdgcn_alignbit(word, word, 30) & 0x3c3c3c3cu;  // even slices * 4
+        const uint32_t rr = __builtin_amdgcn_alignbit(word, word, 2) & 0x3c3c3c3cu;   // odd slices * 4
+        uint32_t ad[8];
+        ad[0] = byte_add<0>(lbase, rl);
+        ad[1] = byte_add<0>(lbase, rr);
+        ad[2] = byte_add<1>(lbase, rl);
+        ad[3] = byte_add<1>(lbase, rr);
+        ad[4] = byte_add<2>(lbase, rl);
+        ad[5] = byte_add<2>(lbase, rr);
+        ad[6] = byte_add<3>(lbase, rl);
+        ad[7] = byte_add<3>(lbase, rr);
 #pragma unroll
-          for (int n = 0; n < 8; ++n) {
+        for (int n = 0; n < 8; ++n) {
 #pragma unroll
-            for (int b = 0; b < BB; ++b)
-              acc[k][b] += lds_f32(ad[n] + (uint32_t)(j * 8 + n) * ROWB + (uint32_t)b * REG);
-          }
-          // finish this word's adds here: left free, the compiler sinks the
-          // add chains to the end of the loop body and keeps every table
-          // entry of the chunk live, which exhausts the registers
-#pragma unroll
-          for (int b = 0; b < BB; ++b) asm volatile("" : "+v"(acc[k][b]));
+          for (int b = 0; b < BB; ++b) acc[k][b] += lds_f32(ad[n] + (uint32_t)(j * 8 + n) * ROWB + (uint32_t)b * REG);
         }
+        // finish this word's adds here: left free, the compiler sinks the
+        // add chains to the end of the loop body and keeps every table
+        // entry of the chunk live, which exhausts the registers
+#pragma unroll
+        for (int b = 0; b < BB; ++b) asm volatile("" : "+v"(acc[k][b]));
       }
     }
   }
+}
+
+// First index i in [0, n) with rows[i] >= key (n if none), rows ascending:
+// a 64-way search, one probe per lane per round, so about log64(n) + 1
+// dependent loads.  Uniform over the wavefront.
+__device__ inline int lower_bound_rows(rsrc_t rows, int n, int key, int lane) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int step = (hi - lo + 63) / 64;
+    const int p = lo + (lane + 1) * step - 1;
+    const bool ge = p >= hi || (int)ld32(rows, (uint32_t)p * 4u) >= key;
+    const unsigned long long bal = __ballot(ge);
+    const int f = bal ? __builtin_ctzll(bal) : 64;
+    const int nlo = min(lo + f * step, hi);
+    const int nhi = f < 64 ? min(lo + (f + 1) * step - 1, hi) : hi;
+    lo = __builtin_amdgcn_readfirstlane(nlo);
+    hi = __builtin_amdgcn_readfirstlane(nhi);
+  }
+  return lo;
 }
 
 // Register budget.  With one or two bases, one batch column and Q >= 2 the
@@ -159,10 +241,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
     k_prod_f(ProdArgs a) {
   constexpr int RW = 64 / Q;
   constexpr int CW = Q * NWL;
-  constexpr int G = CW * 8;           // 4-column groups per chunk (<= 64: one per lane)
-  constexpr int STEPS = NWL * 8;                // groups per lane quarter
-  constexpr uint32_t ROWB = Q * 64 + 16;        // bytes of one step row: Q tables + 16 pad bytes
-  constexpr uint32_t REG = STEPS * ROWB;        // bytes of one (base, batch column) table set
+  constexpr int G = CW * 8;  // 4-column groups per chunk (<= 64: one per lane)
   extern __shared__ __align__(16) char lds[];
 
   const int lane = threadIdx.x & 63;
@@ -171,8 +250,10 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   const int r = lane % RW;
   const int m = blockIdx.x * RW + r;
   const bool valid = m < a.M;
-  const SignRows<KM> srows = sign_rows<KM, RW>(a, m);  // rows beyond M read padding; their sums are dropped
+  // rows beyond M read padding; their sums are dropped
+  const SignRows<KM> srows = sign_rows<KM, RW>(a.bits, a.plane, a.K, a.ND, m);
   const ActSrc asrc = act_src(a);
+  const rsrc_t alsrc = make_rsrc(a.alpha, a.alpha ? (size_t)a.K * a.M * 4 : 0);
   const bool cs = a.colscale != nullptr;
   const int KX = cs ? a.K : 1;
   const uint32_t wbase_lds = (uint32_t)wv * a.wave_lds;
@@ -195,49 +276,13 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
     fetch_act<KM, BB, XM>(a, asrc, cw0 * 32 + (builder ? lane : 0) * 4, act);
 #pragma unroll
     for (int k = 0; k < KM; ++k)
-      if (base_active<KM>(a, k)) al[k] = __uint_as_float(ld32(asrc.al, (uint32_t)(k * a.M + m) * 4u));
+      if (base_active<KM>(a, k)) al[k] = __uint_as_float(ld32(alsrc, (uint32_t)(k * a.M + m) * 4u));
     load_chunk<KM, NWL>(a, srows, cw0 + q * NWL, cur);
   }
 
   for (int c = 0; c < a.NCH; ++c) {
     const int cw0 = (wv * a.NCH + c) * CW;  // first word of the chunk
-
-    // ---- tables: the 16 signed sums of 4-column group `lane` of the chunk
-    if (builder) {
-      const int qq = lane / STEPS, ii = lane % STEPS;
-      const bool inb = cw0 * 32 + lane * 4 < a.N;
-#pragma unroll
-      for (int kx = 0; kx < KM; ++kx) {
-        if (kx < KX) {
-#pragma unroll
-          for (int b = 0; b < BB; ++b) {
-            float xv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t pk = act.x[0][j >> 1];  // XM != 0: two 16-bit values per word
-              const float d = XM == 1   ? __uint_as_float((j & 1) ? (pk & 0xffff0000u) : (pk << 16))
-                              : XM == 2 ? f16_bits_to_float((uint16_t)((j & 1) ? (pk >> 16) : pk))
-                                        : decode_x(act.x[b][j], a.xdt);
-              xv[j] = (inb && a.b0 + b < a.B) ? d : 0.0f;
-            }
-            if (cs) {
-              xv[0] *= f16_bits_to_float((uint16_t)(act.c[kx].x & 0xffffu));
-              xv[1] *= f16_bits_to_float((uint16_t)(act.c[kx].x >> 16));
-              xv[2] *= f16_bits_to_float((uint16_t)(act.c[kx].y & 0xffffu));
-              xv[3] *= f16_bits_to_float((uint16_t)(act.c[kx].y >> 16));
-            }
-            // entry e = sum_j (2 bit_j(e) - 1) xv[j]: bits 0,1 select the first pair sum, bits 2,3 the second
-            const float p0 = xv[0] + xv[1], m0 = xv[0] - xv[1];
-            const float p1 = xv[2] + xv[3], m1 = xv[2] - xv[3];
-            const float hi[4] = {-p1, m1, -m1, p1};
-            float4* dst = (float4*)(lds + wbase_lds + (uint32_t)(kx * BB + b) * REG + (uint32_t)ii * ROWB +
-                                    (uint32_t)qq * 64);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = make_float4(-p0 + hi[e], m0 + hi[e], -m0 + hi[e], p0 + hi[e]);
-          }
-        }
-      }
-    }
+    if (builder) build_tables<Q, NWL, KM, BB, XM>(asrc, act, KX, lane, cw0 * 32 + lane * 4, lds, wbase_lds);
     // next chunk: activations (their registers are free once the tables are
     // built), then sign words; the next build waits only for the activations
     if (c + 1 < a.NCH) {
@@ -258,22 +303,90 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
     }
   }
 
-  // ---- row scales, then the Q lanes of a row, then the W wavefronts
+  // ---- row scales
   float tot[BB];
 #pragma unroll
   for (int b = 0; b < BB; ++b) tot[b] = 0.0f;
-  if (valid) {
 #pragma unroll
-    for (int k = 0; k < KM; ++k) {
-      if (base_active<KM>(a, k)) {
-        const float alk = a.alpha ? al[k] : 1.0f;
+  for (int k = 0; k < KM; ++k) {
+    if (base_active<KM>(a, k)) {
+      const float alk = a.alpha ? al[k] : 1.0f;
 #pragma unroll
-        for (int b = 0; b < BB; ++b) tot[b] += alk * acc[k][b];
+      for (int b = 0; b < BB; ++b) tot[b] += alk * acc[k][b];
+    }
+  }
+
+  // ---- fused binary low-rank expansion: y += U (alpha_r (.) z), the same
+  // sign product over the r ranks (BiLoCo, "The core idea"); the chunks of
+  // U's r/32 words per row go round-robin over the wavefronts
+  if (a.lr_bits) {
+    const ActSrc ls = lr_src(a);
+    const int ndu = a.lr_r / 32;
+    const SignRows<1> urows = sign_rows<1, RW>(a.lr_bits, a.lr_plane, 1, ndu, m);
+    const int tu = (pad_words(ndu) + CW - 1) / CW;
+    float lacc[1][BB];
+#pragma unroll
+    for (int b = 0; b < BB; ++b) lacc[0][b] = 0.0f;
+    for (int cu = wv; cu < tu; cu += a.W) {
+      ActRaw<1, BB> la;
+      uint32_t uw[1][NWL];
+      fetch_act<1, BB, 0>(a, ls, cu * CW * 32 + (builder ? lane : 0) * 4, la);
+      load_chunk<1, NWL>(a, urows, cu * CW + q * NWL, uw);
+      wave_sync();  // earlier lookups of this wavefront's tables are done
+      if (builder) build_tables<Q, NWL, 1, BB, 0>(ls, la, 1, lane, cu * CW * 32 + lane * 4, lds, wbase_lds);
+      wave_sync();
+      lookup_chunk<Q, NWL, 1, BB>(a, lds, wbase_lds, true, q, uw, lacc);
+    }
+#pragma unroll
+    for (int b = 0; b < BB; ++b) tot[b] += lacc[0][b];
+  }
+
+  // ---- fused protected rows: y[rows[i]] += s_i (q_i . x) (BiSCo-LLM,
+  // "Sensitivity Protection"); the workgroup's protected rows go
+  // round-robin over its wavefronts, each dot product over all 64 lanes
+  if (a.sal_n > 0) {
+    const rsrc_t rs = make_rsrc(a.sal_rows, (size_t)a.sal_n * 4);
+    const rsrc_t qs = make_rsrc(a.sal_q, (size_t)a.sal_n * a.N);
+    const rsrc_t ss = make_rsrc(a.sal_s, (size_t)a.sal_n * 2);
+    const int m0 = blockIdx.x * RW;
+    const int i0 = lower_bound_rows(rs, a.sal_n, m0, lane);
+    const int i1 = lower_bound_rows(rs, a.sal_n, m0 + RW, lane);
+    for (int i = i0 + wv; i < i1; i += a.W) {
+      const int rr = __builtin_amdgcn_readfirstlane((int)ld32(rs, (uint32_t)i * 4u)) - m0;
+      float dot[BB];
+#pragma unroll
+      for (int b = 0; b < BB; ++b) dot[b] = 0.0f;
+      for (int n0 = lane * 16; n0 < a.N; n0 += 1024) {
+        const uint4 qv = ld128(qs, (uint32_t)((size_t)i * a.N + n0));
+        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int b = 0; b < BB; ++b) {
+          const int bb = a.b0 + b < a.B ? a.b0 + b : a.B - 1;
+          const uint32_t esz = a.xdt == BSG_F32 ? 4u : 2u;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const uint32_t off = (uint32_t)((n0 + j) * a.B + bb) * esz;
+            const uint32_t lo = ld16(asrc.x, off), hi = ld16(asrc.x, off + 2);
+            const float xv = decode_x(esz == 4 ? (lo | (hi << 16)) : lo, a.xdt);
+            const float qf = (float)(int8_t)(qw[j >> 2] >> (8 * (j & 3)));
+            dot[b] = __builtin_fmaf(qf, xv, dot[b]);
+          }
+        }
+      }
+      const float sv = f16_bits_to_float((uint16_t)ld16(ss, (uint32_t)i * 2u));
+#pragma unroll
+      for (int b = 0; b < BB; ++b) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) dot[b] += __shfl_xor(dot[b], o);
+        if (r == rr && q == 0 && a.b0 + b < a.B) tot[b] += sv * dot[b];
       }
     }
   }
+
+  // ---- the Q lanes of a row, then the W wavefronts, in a fixed order
 #pragma unroll
   for (int b = 0; b < BB; ++b) {
+    if (!valid) tot[b] = 0.0f;
     if (Q >= 4) tot[b] += __shfl_xor(tot[b], 16);
     if (Q >= 2) tot[b] += __shfl_xor(tot[b], 32);
   }

@@ -82,6 +82,18 @@ struct ProdArgs {
   int K, M, N, ND, B, b0, xdt, accumulate, W, NCH;
   int xvec;                  // x 16-byte and colscale 8-byte aligned: vector loads
   uint32_t wave_lds;
+  // Fused terms of bsg_linear (float path; NULL / 0 when absent):
+  //   y += U (lr_scale (.) lr_z)        binary low-rank expansion, z = V x precomputed
+  //   y[sal_rows[i]] += sal_s[i] * (sal_q[i] . x)   protected int8 rows
+  const uint32_t* lr_bits;   // U: device layout, M x lr_r signs, or NULL
+  size_t lr_plane;
+  const float* lr_z;         // [lr_r][B]
+  const uint16_t* lr_scale;  // fp16 [lr_r]
+  int lr_r;                  // rank, a multiple of 32
+  int sal_n;                 // protected rows (0: none)
+  const int32_t* sal_rows;   // [sal_n], ascending
+  const int8_t* sal_q;       // [sal_n][N]
+  const uint16_t* sal_s;     // fp16 [sal_n]
 };
 
 hipError_t launch_prod_f(const ProdArgs& a, const ProdPlan& p, hipStream_t s);

@@ -66,14 +66,14 @@ struct SignRows {
   uint32_t row_off;  // byte offset of this lane's row in a tile: (m % 64) * 16
 };
 template <int KM, int RW>
-__device__ inline SignRows<KM> sign_rows(const ProdArgs& a, int m) {
+__device__ inline SignRows<KM> sign_rows(const uint32_t* bits, size_t plane, int K, int ND, int m) {
   SignRows<KM> s;
   const int rb = (int)(blockIdx.x * RW) >> 6;
-  const size_t blk = (size_t)64 * pad_words(a.ND);  // words of one row block
+  const size_t blk = (size_t)64 * pad_words(ND);  // words of one row block
   s.row_off = (uint32_t)(m & 63) * 16u;
 #pragma unroll
   for (int k = 0; k < KM; ++k)
-    s.r[k] = make_rsrc(a.bits + (size_t)(k < a.K ? k : 0) * a.plane + (size_t)rb * blk, blk * 4);
+    s.r[k] = make_rsrc(bits + (size_t)(k < K ? k : 0) * plane + (size_t)rb * blk, blk * 4);
   return s;
 }
 

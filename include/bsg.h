@@ -248,6 +248,32 @@ BSG_API bsg_status salient_int8_apply(const int32_t* rows, int ns, const int8_t*
                               const void* x, int x_dtype, int B, float* y,
                               void* stream);
 
+/*
+ * bsg_linear -- the whole layer in one pass over x: the binary bases
+ * (FluxBin Sec. 3.1/3.2), the binary low-rank correction (BiLoCo "The core
+ * idea") and the protected int8 rows (BiSCo-LLM "Sensitivity Protection"):
+ *   y[m,b] (= or +=) bs_gemv term + sum_j su(m,j) alpha_r[j] (v_j . x_b)
+ *                    + [m = rows[i]] s_i (q_i . x_b)
+ * Arguments as in bs_gemv, binlr_apply and salient_int8_apply, with:
+ *   U_bits, V_bits, alpha_r: all NULL with r == 0 (no correction), or all
+ *     given with r > 0, r % 32 == 0;
+ *   rows, q, s_f16: all NULL with ns == 0, or all given with ns > 0; rows
+ *     strictly ascending, each in [0, M); q 16-byte aligned.
+ *   workspace (device) >= bsg_linear_workspace_bytes(r, B) (may be NULL when
+ *     that is 0).
+ * Two launches when r > 0 (z = V x, then everything else in one kernel that
+ * reads x once per workgroup), one otherwise.  Fixed-order fp32 sums; within
+ * the sum of the three terms' bounds above.
+ */
+BSG_API size_t bsg_linear_workspace_bytes(int r, int B);
+BSG_API bsg_status bsg_linear(const uint32_t* bits, int K, int M, int N, const float* alpha,
+                      const uint16_t* colscale, const uint32_t* U_bits,
+                      const uint32_t* V_bits, const uint16_t* alpha_r, int r,
+                      const int32_t* rows, int ns, const int8_t* q,
+                      const uint16_t* s_f16, const void* x, int x_dtype, int B,
+                      float* y, int accumulate, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

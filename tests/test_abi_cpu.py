@@ -123,7 +123,7 @@ def test_bs_gemv_i8_validation():
     assert f(acc=None, y=None) == ENULL
     assert f(xq=None) == ENULL
     assert f(y=A16d, sx=None) == ENULL
-    assert f(M=0) == OK
+    assert f(M=0, ns=0) == OK
 
 
 @fake_ptrs
@@ -138,6 +138,39 @@ def test_binlr_and_salient_validation():
     assert L.salient_int8_apply(A16, -1, A16b, A16c, 64, 64, A16d, 2, 1, A16, None) == ESHAPE
     assert L.salient_int8_apply(A16, 0, A16b, A16c, 64, 64, A16d, 2, 1, A16, None) == OK
     assert L.salient_int8_apply(A16 + 2, 3, A16b, A16c, 64, 64, A16d, 2, 1, A16, None) == EALIGN
+
+
+@fake_ptrs
+def test_bsg_linear_validation():
+    L = bsg.lib()
+
+    def f(**kw):
+        d = dict(bits=A16, K=2, M=128, N=256, alpha=A16b, cs=None, U=A16c, V=A16d, ar=A16, r=32, rows=A16b,
+                 ns=3, q=A16c, s=A16d, x=A16, dt=2, B=1, y=A16b, acc=0, ws=None, wsn=0)
+        d.update(kw)
+        return L.bsg_linear(d["bits"], d["K"], d["M"], d["N"], d["alpha"], d["cs"], d["U"], d["V"], d["ar"], d["r"],
+                            d["rows"], d["ns"], d["q"], d["s"], d["x"], d["dt"], d["B"], d["y"], d["acc"], d["ws"],
+                            d["wsn"], None)
+    assert f(dt=9) == EDTYPE
+    assert f(N=48) == ESHAPE
+    assert f(r=40) == ESHAPE
+    assert f(r=-32) == ESHAPE
+    assert f(ns=-1) == ESHAPE
+    assert f(ns=129) == ESHAPE                   # more protected rows than rows
+    assert f(K=9) == ESHAPE
+    assert f(M=0, ns=0) == OK
+    assert f(U=None) == ENULL                    # r > 0 needs U, V and alpha_r
+    assert f(ar=None) == ENULL
+    assert f(q=None) == ENULL                    # ns > 0 needs rows, q and s
+    assert f(alpha=None) == ENULL
+    assert f(q=A16c + 8) == EALIGN               # q rows are read 16 bytes at a time
+    assert f(rows=A16b + 2) == EALIGN
+    assert f(U=A16c + 4) == EALIGN
+    assert f(ws=None) == EWS                     # r > 0 needs the z workspace
+    assert f(ws=0x500000, wsn=64) == EWS
+    assert L.bsg_linear_workspace_bytes(32, 1) >= 32 * 4
+    assert L.bsg_linear_workspace_bytes(0, 1) == 0
+    assert L.bsg_linear_workspace_bytes(40, 1) == 0
 
 
 @fake_ptrs

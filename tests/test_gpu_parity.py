@@ -238,6 +238,96 @@ def test_salient_apply_matches_oracle(case):
     assert not y.cpu().numpy()[other].any()
 
 
+# ------------------------------------------------------------------ fused layer
+LINEAR_CASES = [
+    # K, M, N, B, colscale, x dtype, rank r, protected rows ns
+    (2, 300, 544, 1, True, "bf16", 64, 5),
+    (3, 5120, 5120, 1, False, "bf16", 512, 51),
+    (2, 1000, 1024, 4, False, "f32", 32, 10),
+    (1, 64, 32, 1, False, "f16", 32, 64),
+    (2, 200, 256, 16, True, "bf16", 96, 3),
+    (2, 700, 4096, 2, False, "bf16", 0, 7),
+    (2, 17000, 512, 1, False, "bf16", 128, 170),
+    (2, 129, 1056, 3, True, "bf16", 32, 0),
+]
+
+
+def _linear_inputs(case):
+    K, M, N, B, cs, dt, r, ns = case
+    seed = 104729 + K * 7919 + M * 31 + N + B + r + ns
+    L = synth.random_bits(seed, K, M, N)
+    alpha, csb = synth.random_scales(seed, K, M, N, cs)
+    x = synth.random_x(seed, N, B, dt, "student_t3")
+    g = np.random.default_rng(seed)
+    u = np.where(g.integers(0, 2, (M, r)) == 1, 1.0, -1.0).astype(np.float32)
+    v = np.where(g.integers(0, 2, (r, N)) == 1, 1.0, -1.0).astype(np.float32)
+    ar = np.abs(g.normal(0, 0.005, r)).astype(np.float16).view(np.uint16)
+    rows = np.sort(g.choice(M, ns, replace=False)).astype(np.int32)
+    q = g.integers(-127, 128, (ns, N)).astype(np.int8)
+    sv = g.uniform(1e-4, 1e-3, ns).astype(np.float16).view(np.uint16)
+    alpha[:, rows] = 0.0  # protected rows replace the binary part
+    return L, alpha, csb, x, u, v, ar, rows, q, sv
+
+
+def _run_linear(case, y0=None):
+    K, M, N, B, cs, dt, r, ns = case
+    L, alpha, csb, x, u, v, ar, rows, q, sv = _linear_inputs(case)
+    bits = _layout(L, K, M, N)
+    lowrank = None
+    if r:
+        lowrank = (bsg.bsq_pack_signs(to_dev(u)), bsg.bsq_pack_signs(to_dev(v)), f16_dev(ar), r)
+    salient = (to_dev(rows), to_dev(q), f16_dev(sv)) if ns else None
+    y = None if y0 is None else to_dev(y0)
+    y = bsg.bsg_linear(bits, K, M, N, to_dev(alpha), x_dev(x, dt), colscale=f16_dev(csb) if cs else None,
+                       lowrank=lowrank, salient=salient, y=y, accumulate=y0 is not None)
+    torch.cuda.synchronize()
+    ref = oracle.sign_gemv(L, K, M, N, alpha, x, csb)
+    if r:
+        ref = ref + oracle.binlr(oracle.pack_signs(u), oracle.pack_signs(v), ar, r, M, N, x)
+    if ns:
+        ref = ref + oracle.salient(rows, q, sv, M, N, x)
+    if y0 is not None:
+        ref = ref + y0
+    tol = oracle.tolerance(x, alpha=alpha, colscale_f16=csb, alpha_r_f16=ar if r else None,
+                           rows=rows if ns else None, q=q if ns else None, s_f16=sv if ns else None, M=M)
+    return y, ref, tol
+
+
+@pytest.mark.parametrize("case", LINEAR_CASES, ids=lambda c: "K%d_M%d_N%d_B%d_cs%d_%s_r%d_ns%d" % c)
+def test_bsg_linear_matches_oracle(case):
+    say("bsg_linear", case)
+    y, ref, tol = _run_linear(case)
+    check_close(y.cpu().numpy(), ref, tol, "bsg_linear %s" % (case,))
+
+
+def test_bsg_linear_accumulates_and_reduces_to_bs_gemv():
+    case = (2, 300, 544, 2, True, "bf16", 64, 5)
+    say("bsg_linear accumulate", case)
+    y0 = np.linspace(-1, 1, 300 * 2, dtype=np.float32).reshape(300, 2)
+    y, ref, tol = _run_linear(case, y0)
+    check_close(y.cpu().numpy(), ref, tol + 1e-6, "bsg_linear accumulate")
+    # without a correction or protected rows it is bs_gemv, bit for bit
+    K, M, N, B, cs, dt = 2, 1000, 4096, 1, True, "bf16"
+    L, alpha, csb, x = _gemv_inputs((K, M, N, B, cs, dt, "normal"))
+    bits = _layout(L, K, M, N)
+    args = (bits, K, M, N, to_dev(alpha), x_dev(x, dt))
+    y1 = bsg.bs_gemv(*args, colscale=f16_dev(csb))
+    y2 = bsg.bsg_linear(*args, colscale=f16_dev(csb))
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("qw", [(1, 1), (2, 3), (4, 16), (2, 8)], ids=lambda c: "Q%d_W%d" % c)
+def test_bsg_linear_every_decomposition(qw, monkeypatch):
+    # few wavefronts: several low-rank chunks and protected rows per wavefront
+    monkeypatch.setenv("BSG_Q", str(qw[0]))
+    monkeypatch.setenv("BSG_WAVES", str(qw[1]))
+    for case in [(2, 300, 544, 1, True, "bf16", 256, 40), (3, 130, 1024, 3, False, "f32", 96, 9)]:
+        say("bsg_linear forced", qw, case)
+        y, ref, tol = _run_linear(case)
+        check_close(y.cpu().numpy(), ref, tol, "bsg_linear forced %s %s" % (qw, case))
+
+
 # ------------------------------------------------------------------ packing
 PACK_CASES = [(256, 256, 1, False), (320, 544, 3, False), (130, 96, 2, True), (4096, 4096, 2, True),
               (1, 32, 2, True), (70, 4096, 4, True)]

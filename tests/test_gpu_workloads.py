@@ -4,9 +4,10 @@ plans the benchmark times.
 
 Per workload shape: GPU packing must equal the oracle's packing bit for bit
 (sign bits, row scales, column scales, protected rows and their int8 codes);
-the full product  y = bases + binary low-rank + protected rows  must lie within
-the per-output bound at every output for batch 1, and on a seeded sample of
-rows for the larger batches.
+the full product  y = bases + binary low-rank + protected rows, computed both
+by the separate calls and by the fused bsg_linear, must lie within the
+per-output bound at every output for batch 1, and on a seeded sample of rows
+for the larger batches.
 """
 import numpy as np
 import pytest
@@ -97,3 +98,10 @@ def test_workload_end_to_end(wid, part):
         tol = oracle.tolerance(x, M=len(sel), **tolkw)
         err, ratio = check_close(yh[sel], ref, tol, "%s/%s B=%d" % (w.name, sh.name, B))
         say("  max err %.3e, max err/tol %.3f" % (err, ratio))
+        # the same layer through the fused entry point
+        yf = bsg.bsg_linear(bits, K, M, N, alpha, xd, colscale=cs,
+                            lowrank=(Ub, Vb, ard, lr.r) if lr is not None else None,
+                            salient=(rows, q, s) if ns else None)
+        torch.cuda.synchronize()
+        err, ratio = check_close(yf.cpu().numpy()[sel], ref, tol, "fused %s/%s B=%d" % (w.name, sh.name, B))
+        say("  fused: max err %.3e, max err/tol %.3f" % (err, ratio))
