@@ -33,6 +33,12 @@ size_t dtype_size(int dt) { return dt == BSG_F32 ? 4 : 2; }
 
 bool bad_n(int N) { return N <= 0 || (N % 32) != 0; }
 
+// Every operand of one product is addressed with 32-bit byte offsets:
+// K*M row scales, N*B activations and K*N column scales below 2^30 elements.
+bool too_big(int K, int M, int N, int B) {
+  return (size_t)K * M >= (1u << 30) || (size_t)N * B >= (1u << 30) || (size_t)K * N >= (1u << 30);
+}
+
 bsg_status hip_status(hipError_t e) { return e == hipSuccess ? BSG_OK : BSG_ERR_HIP; }
 
 // binlr workspace: z, fp32 [r][B]
@@ -157,7 +163,7 @@ bsg_status bsg_layout_to_logical(const uint32_t* bits, int K, int M, int N, uint
 bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const float* alpha, const uint16_t* colscale,
                    const void* x, int x_dtype, int B, float* y, int accumulate, void* stream) {
   if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
-  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || B < 1 || B > kMaxB) return BSG_ERR_SHAPE;
+  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || B < 1 || B > kMaxB || too_big(K, M, N, B)) return BSG_ERR_SHAPE;
   if (M == 0) return BSG_OK;
   if (!bits || !alpha || !x || !y) return BSG_ERR_NULL;
   if (misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(colscale, 2) ||
@@ -184,7 +190,8 @@ bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const float* alpha
 
 bsg_status bs_gemv_i8(const uint32_t* bits, int K, int M, int N, const float* alpha, const int8_t* xq,
                       const float* sx, int B, int32_t* acc, float* y, int accumulate, void* stream) {
-  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || N > (1 << 24) || B < 1 || B > kMaxB) return BSG_ERR_SHAPE;
+  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || N > (1 << 24) || B < 1 || B > kMaxB || too_big(K, M, N, B))
+    return BSG_ERR_SHAPE;
   if (M == 0) return BSG_OK;
   if (!bits || !xq || (!acc && !y) || (y && (!alpha || !sx))) return BSG_ERR_NULL;
   if (misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(sx, 4) || misaligned(acc, 4) || misaligned(y, 4))
@@ -211,7 +218,9 @@ bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uin
                        int N, const void* x, int x_dtype, int B, float* y, void* workspace, size_t workspace_bytes,
                        void* stream) {
   if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
-  if (r <= 0 || (r % 32) != 0 || M < 0 || bad_n(N) || B < 1 || B > kMaxB) return BSG_ERR_SHAPE;
+  if (r <= 0 || (r % 32) != 0 || M < 0 || bad_n(N) || B < 1 || B > kMaxB || too_big(1, M, N, B) ||
+      too_big(1, r, r, B))
+    return BSG_ERR_SHAPE;
   if (M == 0) return BSG_OK;
   if (!U_bits || !V_bits || !alpha_r || !x || !y) return BSG_ERR_NULL;
   if (misaligned(U_bits, 16) || misaligned(V_bits, 16) || misaligned(alpha_r, 2) ||
@@ -270,7 +279,7 @@ bsg_status bsg_linear(const uint32_t* bits, int K, int M, int N, const float* al
                       void* stream) {
   if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
   if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || B < 1 || B > kMaxB || r < 0 || (r % 32) != 0 || ns < 0 ||
-      ns > M)
+      ns > M || too_big(K, M, N, B) || too_big(1, r, r, B) || (size_t)ns * N >= (1u << 30))
     return BSG_ERR_SHAPE;
   if (M == 0) return BSG_OK;
   if (!bits || !alpha || !x || !y) return BSG_ERR_NULL;

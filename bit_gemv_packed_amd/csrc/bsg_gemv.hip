@@ -50,8 +50,8 @@ struct ActSrc {
 };
 __device__ inline ActSrc act_src(const ProdArgs& a) {
   ActSrc s;
-  s.x = make_rsrc(a.x, (size_t)a.N * a.B * (a.xdt == BSG_F32 ? 4 : 2));
-  s.c = make_rsrc(a.colscale, a.colscale ? (size_t)a.K * a.N * 2 : 0);
+  s.x = make_rsrc(a.x, a.x_bytes);
+  s.c = make_rsrc(a.colscale, a.cs_bytes);
   s.N = a.N;
   s.B = a.B;
   s.b0 = a.b0;
@@ -172,43 +172,49 @@ __device__ inline void build_tables(const ActSrc& s, const ActRaw<KM, BB>& act, 
 
 // Lookups of one chunk: acc[k][b] += table entry of each 4-bit slice.  Words
 // beyond ND are zero words (padding) or read 0 (beyond the row block) and
-// their columns' tables are zero, so they add +-0 and need no guard.
+// their columns' tables are zero, so they add +-0 and need no guard.  Word j
+// of every base is looked up together: 8K independent LDS reads in flight
+// and K independent add chains.
 template <int Q, int NWL, int KM, int BB>
 __device__ inline void lookup_chunk(const ProdArgs& a, const char* lds, uint32_t wbase_lds, bool cs, int q,
                                     const uint32_t (&cur)[KM][NWL], float (&acc)[KM][BB]) {
   constexpr uint32_t ROWB = Q * 64 + 16;             // bytes of one step row of tables
   constexpr uint32_t REG = NWL * 8 * ROWB;           // bytes of one (base, batch column) table set
+  uint32_t lbase[KM];
 #pragma unroll
-  for (int k = 0; k < KM; ++k) {
-    if (base_active<KM>(a, k)) {
-      const uint32_t lbase =
-          (uint32_t)(uintptr_t)(lds + wbase_lds + (uint32_t)(cs ? k : 0) * BB * REG + (uint32_t)q * 64);
+  for (int k = 0; k < KM; ++k)
+    lbase[k] = (uint32_t)(uintptr_t)(lds + wbase_lds + (uint32_t)(cs ? k : 0) * BB * REG + (uint32_t)q * 64);
 #pragma unroll
-      for (int j = 0; j < NWL; ++j) {
+  for (int j = 0; j < NWL; ++j) {
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (base_active<KM>(a, k)) {
         const uint32_t word = cur[k][j];
         const uint32_t rl = __builtin_amdgcn_alignbit(word, word, 30) & 0x3c3c3c3cu;  // even slices * 4
         const uint32_t rr = __builtin_amdgcn_alignbit(word, word, 2) & 0x3c3c3c3cu;   // odd slices * 4
         uint32_t ad[8];
-        ad[0] = byte_add<0>(lbase, rl);
-        ad[1] = byte_add<0>(lbase, rr);
-        ad[2] = byte_add<1>(lbase, rl);
-        ad[3] = byte_add<1>(lbase, rr);
-        ad[4] = byte_add<2>(lbase, rl);
-        ad[5] = byte_add<2>(lbase, rr);
-        ad[6] = byte_add<3>(lbase, rl);
-        ad[7] = byte_add<3>(lbase, rr);
+        ad[0] = byte_add<0>(lbase[k], rl);
+        ad[1] = byte_add<0>(lbase[k], rr);
+        ad[2] = byte_add<1>(lbase[k], rl);
+        ad[3] = byte_add<1>(lbase[k], rr);
+        ad[4] = byte_add<2>(lbase[k], rl);
+        ad[5] = byte_add<2>(lbase[k], rr);
+        ad[6] = byte_add<3>(lbase[k], rl);
+        ad[7] = byte_add<3>(lbase[k], rr);
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
 #pragma unroll
           for (int b = 0; b < BB; ++b) acc[k][b] += lds_f32(ad[n] + (uint32_t)(j * 8 + n) * ROWB + (uint32_t)b * REG);
         }
-        // finish this word's adds here: left free, the compiler sinks the
-        // add chains to the end of the loop body and keeps every table
-        // entry of the chunk live, which exhausts the registers
-#pragma unroll
-        for (int b = 0; b < BB; ++b) asm volatile("" : "+v"(acc[k][b]));
       }
     }
+    // finish word j's adds here: left free, the compiler sinks the add chains
+    // to the end of the loop body and keeps every table entry of the chunk
+    // live, which exhausts the registers
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+#pragma unroll
+      for (int b = 0; b < BB; ++b) asm volatile("" : "+v"(acc[k][b]));
   }
 }
 
@@ -244,6 +250,11 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   constexpr int G = CW * 8;  // 4-column groups per chunk (<= 64: one per lane)
   extern __shared__ __align__(16) char lds[];
 
+  // every argument the prologue needs, in registers before anything else:
+  // one batch of scalar loads and one wait, ahead of the first vector loads
+  asm volatile("" ::"s"(a.bits), "s"(a.alpha), "s"(a.colscale), "s"(a.x), "s"(a.plane), "s"(a.K), "s"(a.M),
+               "s"(a.N), "s"(a.ND), "s"(a.B), "s"(a.b0), "s"(a.xdt), "s"(a.NCH), "s"(a.wave_lds), "s"(a.x_bytes),
+               "s"(a.cs_bytes), "s"(a.al_bytes));
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wavefront index (uniform)
   const int q = lane / RW;
@@ -253,7 +264,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   // rows beyond M read padding; their sums are dropped
   const SignRows<KM> srows = sign_rows<KM, RW>(a.bits, a.plane, a.K, a.ND, m);
   const ActSrc asrc = act_src(a);
-  const rsrc_t alsrc = make_rsrc(a.alpha, a.alpha ? (size_t)a.K * a.M * 4 : 0);
+  const rsrc_t alsrc = make_rsrc(a.alpha, a.al_bytes);
   const bool cs = a.colscale != nullptr;
   const int KX = cs ? a.K : 1;
   const uint32_t wbase_lds = (uint32_t)wv * a.wave_lds;
@@ -265,43 +276,49 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
 #pragma unroll
     for (int b = 0; b < BB; ++b) acc[k][b] = 0.0f;
 
-  // First chunk: activations and column scales, row scales, then sign words,
-  // all in flight at once.  Loads complete in issue order, so the table build
-  // (which needs only the activations) need not wait for the sign words.
-  uint32_t cur[KM][NWL], nxt[KM][NWL];
+  // First chunk: activations and column scales, row scales, then the sign
+  // words of the first two chunks, all in flight at once.  Loads complete in
+  // issue order, so the table build (which needs only the activations) need
+  // not wait for the sign words.  Sign words stay two chunks ahead of the
+  // lookups, in three buffers used round-robin (the loop is unrolled by
+  // three: a register copy between buffers would wait for the loads in
+  // flight); activations stay one chunk ahead of the build.
+  uint32_t wb0[KM][NWL], wb1[KM][NWL], wb2[KM][NWL];
   ActRaw<KM, BB> act;
   float al[KM];
-  {
-    const int cw0 = wv * a.NCH * CW;
-    fetch_act<KM, BB, XM>(a, asrc, cw0 * 32 + (builder ? lane : 0) * 4, act);
+  const int c0 = wv * a.NCH;  // this wavefront's first chunk
+  fetch_act<KM, BB, XM>(a, asrc, c0 * CW * 32 + (builder ? lane : 0) * 4, act);
 #pragma unroll
-    for (int k = 0; k < KM; ++k)
-      if (base_active<KM>(a, k)) al[k] = __uint_as_float(ld32(alsrc, (uint32_t)(k * a.M + m) * 4u));
-    load_chunk<KM, NWL>(a, srows, cw0 + q * NWL, cur);
-  }
+  for (int k = 0; k < KM; ++k)
+    if (base_active<KM>(a, k)) al[k] = __uint_as_float(ld32(alsrc, (uint32_t)(k * a.M + m) * 4u));
+  // Prefetches past the wavefront's last chunk re-read that chunk (a cache
+  // hit, no HBM traffic) instead of being skipped: unconditional loads keep
+  // the compiler's load counting exact, so every wait is for the oldest load.
+  const int clast = a.NCH - 1;
+  load_chunk<KM, NWL>(a, srows, c0 * CW + q * NWL, wb0);
+  load_chunk<KM, NWL>(a, srows, (c0 + min(1, clast)) * CW + q * NWL, wb1);
 
-  for (int c = 0; c < a.NCH; ++c) {
-    const int cw0 = (wv * a.NCH + c) * CW;  // first word of the chunk
+  // one chunk: build its tables, issue the next chunk's activations and the
+  // sign words two chunks ahead (into `ahead`), look up `cur`
+  auto chunk = [&](int c, const uint32_t(&cur)[KM][NWL], uint32_t(&ahead)[KM][NWL]) {
+    const int cw0 = (c0 + c) * CW;  // first word of the chunk
     if (builder) build_tables<Q, NWL, KM, BB, XM>(asrc, act, KX, lane, cw0 * 32 + lane * 4, lds, wbase_lds);
-    // next chunk: activations (their registers are free once the tables are
-    // built), then sign words; the next build waits only for the activations
-    if (c + 1 < a.NCH) {
-      fetch_act<KM, BB, XM>(a, asrc, (cw0 + CW) * 32 + (builder ? lane : 0) * 4, act);
-      load_chunk<KM, NWL>(a, srows, cw0 + CW + q * NWL, nxt);
-    }
+    fetch_act<KM, BB, XM>(a, asrc, (c0 + min(c + 1, clast)) * CW * 32 + (builder ? lane : 0) * 4, act);
+    load_chunk<KM, NWL>(a, srows, (c0 + min(c + 2, clast)) * CW + q * NWL, ahead);
     wave_sync();  // the tables are private to this wavefront
-
-    // ---- lookups: one table read and one add per 4 weights
     lookup_chunk<Q, NWL, KM, BB>(a, lds, wbase_lds, cs, q, cur, acc);
-
-    if (c + 1 < a.NCH) {
-      wave_sync();  // the next chunk's tables overwrite these
-#pragma unroll
-      for (int k = 0; k < KM; ++k)
-#pragma unroll
-        for (int j = 0; j < NWL; ++j) cur[k][j] = nxt[k][j];
-    }
+    wave_sync();  // the next chunk's tables overwrite these
+  };
+  // No branch inside the loop body: the compiler's load counting at the
+  // back edge stays exact.  The last one or two chunks run after it.
+  int c = 0;
+  for (; c + 3 <= a.NCH; c += 3) {
+    chunk(c, wb0, wb2);
+    chunk(c + 1, wb1, wb0);
+    chunk(c + 2, wb2, wb1);
   }
+  if (c < a.NCH) chunk(c, wb0, wb2);
+  if (c + 1 < a.NCH) chunk(c + 1, wb1, wb0);
 
   // ---- row scales
   float tot[BB];
@@ -359,17 +376,30 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
       for (int n0 = lane * 16; n0 < a.N; n0 += 1024) {
         const uint4 qv = ld128(qs, (uint32_t)((size_t)i * a.N + n0));
         const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-        for (int b = 0; b < BB; ++b) {
-          const int bb = a.b0 + b < a.B ? a.b0 + b : a.B - 1;
-          const uint32_t esz = a.xdt == BSG_F32 ? 4u : 2u;
+        if (XM != 0) {  // 16 aligned 16-bit activations: two 16-byte loads
+          const uint4 x0 = ld128(asrc.x, (uint32_t)n0 * 2u), x1 = ld128(asrc.x, (uint32_t)n0 * 2u + 16u);
+          const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const uint32_t off = (uint32_t)((n0 + j) * a.B + bb) * esz;
-            const uint32_t lo = ld16(asrc.x, off), hi = ld16(asrc.x, off + 2);
-            const float xv = decode_x(esz == 4 ? (lo | (hi << 16)) : lo, a.xdt);
+            const uint32_t pk = xw[j >> 1];
+            const float xv = XM == 1 ? __uint_as_float((j & 1) ? (pk & 0xffff0000u) : (pk << 16))
+                                     : f16_bits_to_float((uint16_t)((j & 1) ? (pk >> 16) : pk));
             const float qf = (float)(int8_t)(qw[j >> 2] >> (8 * (j & 3)));
-            dot[b] = __builtin_fmaf(qf, xv, dot[b]);
+            dot[0] = __builtin_fmaf(qf, xv, dot[0]);
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < BB; ++b) {
+            const int bb = a.b0 + b < a.B ? a.b0 + b : a.B - 1;
+            const uint32_t esz = a.xdt == BSG_F32 ? 4u : 2u;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const uint32_t off = (uint32_t)((n0 + j) * a.B + bb) * esz;
+              const uint32_t lo = ld16(asrc.x, off), hi = ld16(asrc.x, off + 2);
+              const float xv = decode_x(esz == 4 ? (lo | (hi << 16)) : lo, a.xdt);
+              const float qf = (float)(int8_t)(qw[j >> 2] >> (8 * (j & 3)));
+              dot[b] = __builtin_fmaf(qf, xv, dot[b]);
+            }
           }
         }
       }
@@ -475,9 +505,13 @@ static hipError_t dispatch_f(const ProdArgs& a, const ProdPlan& p, hipStream_t s
 
 hipError_t launch_prod_f(const ProdArgs& a0, const ProdPlan& p0, hipStream_t st) {
   ProdPlan p = p0;
+  ProdArgs as = a0;
+  as.x_bytes = (uint32_t)((size_t)a0.N * a0.B * (a0.xdt == BSG_F32 ? 4 : 2));
+  as.cs_bytes = a0.colscale ? (uint32_t)((size_t)a0.K * a0.N * 2) : 0u;
+  as.al_bytes = a0.alpha ? (uint32_t)((size_t)a0.K * a0.M * 4) : 0u;
   p.XM = (a0.B == 1 && a0.xvec && a0.xdt != BSG_F32) ? (a0.xdt == BSG_BF16 ? 1 : 2) : 0;
   for (int c = 0; c < p.nlaunch; ++c) {
-    ProdArgs a = a0;
+    ProdArgs a = as;
     a.b0 = c * p.BB;
     a.W = p.W;
     a.NCH = p.NCH;

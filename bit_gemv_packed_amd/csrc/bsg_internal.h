@@ -70,18 +70,26 @@ struct ProdPlan {
 ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool int8_mode);
 
 struct ProdArgs {
+  // Read by the prologue of every product kernel: kept together at the front
+  // so that they arrive in one batch of scalar loads.
   const uint32_t* bits;
   const float* alpha;        // fp32 [K][M], or NULL
   const uint16_t* colscale;  // fp16 [K][N], or NULL
   const void* x;             // [N][B] of dtype xdt (float path)
-  const int8_t* xq;          // [N][B] (int8 path)
-  const float* sx;           // [B] (int8 path)
-  int32_t* acc;              // [K][M][B] or NULL (int8 path)
   float* y;                  // [M][B] or NULL (int8 path)
   size_t plane;
-  int K, M, N, ND, B, b0, xdt, accumulate, W, NCH;
-  int xvec;                  // x 16-byte and colscale 8-byte aligned: vector loads
+  int K, M, N, ND;
+  int B, b0, xdt, accumulate;
+  int W, NCH;
   uint32_t wave_lds;
+  // operand sizes in bytes (0 for an absent operand), set by the launcher so
+  // that the kernel prologue has no branches
+  uint32_t x_bytes, cs_bytes, al_bytes;
+  int xvec;                  // x 16-byte and colscale 8-byte aligned: vector loads
+  // int8 path
+  const int8_t* xq;          // [N][B]
+  const float* sx;           // [B]
+  int32_t* acc;              // [K][M][B] or NULL
   // Fused terms of bsg_linear (float path; NULL / 0 when absent):
   //   y += U (lr_scale (.) lr_z)        binary low-rank expansion, z = V x precomputed
   //   y[sal_rows[i]] += sal_s[i] * (sal_q[i] . x)   protected int8 rows

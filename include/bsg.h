@@ -37,7 +37,9 @@
  *  - Sign buffers and workspaces must be 16-byte aligned; every other
  *    pointer must be aligned to its element size (BSG_ERR_ALIGN).
  *  - N (the input dimension) must be a positive multiple of 32; M >= 0; an
- *    M of 0 is a no-op returning BSG_OK.
+ *    M of 0 is a no-op returning BSG_OK.  Each product addresses its
+ *    operands with 32-bit offsets: K*M, N*B and K*N must stay below 2^30
+ *    (BSG_ERR_SHAPE otherwise).
  *
  * Logical sign layout: word w of row m of base k holds columns 32w..32w+31,
  * bit j of the word is column 32w+j.  A set bit is +1, a clear bit is -1.
