@@ -163,6 +163,142 @@ def load_traffic():
     return t.get("bytes_per_launch")
 
 
+# ------------------------------------------------------------------ every row of the path
+
+def _graph_us(step, steps, warmup):
+    """Mean µs per call of step(i) over `steps` calls replayed from one HIP graph."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(warmup + i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def run_rows(steps, warmup):
+    """Time every row of the hot path on the pages' projection shapes (synthetic operands, >= 512 MiB
+    of rotating weight copies per case, HIP-graph replay).  Prints one JSON line per case."""
+    import torch
+    import bit_gemv_packed_amd as bsg
+    from bit_gemv_packed_amd import synth
+    dev = torch.device("cuda:0")
+    out = []
+
+    def emit(row, op, shape, us, nbytes, **extra):
+        d = {"row": row, "op": op, "shape": shape, "us": round(us, 3), "alg_bytes": int(nbytes),
+             "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / (us * 1e-6) / 8e12, 2)}
+        d.update(extra)
+        print(json.dumps(d), flush=True)
+        out.append(d)
+
+    def copies(nbytes_per_copy):
+        return max(2, -(-ROTATE_BYTES // max(1, nbytes_per_copy)))
+
+    def rand_bits(K, M, N, n):
+        return torch.randint(-2**31, 2**31 - 1, (n, bsg.layout_words(K, M, N)), dtype=torch.int32, device=dev)
+
+    def xs(N, B, n, dt=torch.bfloat16):
+        return torch.randn((n, N, B), device=dev).to(dt)
+
+    # a1-a3, a7: the sign product
+    shapes = [("q/o 4096x4096", 4096, 4096, 2, False), ("k/v 1024x4096", 1024, 4096, 2, False),
+              ("gate/up 14336x4096", 14336, 4096, 2, False), ("down 4096x14336", 4096, 14336, 2, False),
+              ("4096x4096 colscale", 4096, 4096, 2, True), ("5120x5120 K=3", 5120, 5120, 3, False),
+              ("13824x5120", 13824, 5120, 2, False), ("5120x13824", 5120, 13824, 2, False),
+              ("28672x8192", 28672, 8192, 2, False)]
+    for name, M, N, K, cs in shapes:
+        for B in ((1, 4, 16) if name.split()[0] in ("q/o", "gate/up", "down") else (1,)):
+            wb = K * M * N // 8 + 4 * K * M + (2 * K * N if cs else 0)
+            n = copies(wb)
+            bits = rand_bits(K, M, N, n)
+            alpha = torch.rand((n, K, M), device=dev) * 0.02
+            csd = (torch.rand((n, K, N), device=dev) + 0.5).half().view(torch.int16) if cs else None
+            x = xs(N, B, n)
+            y = torch.empty((n, M, B), device=dev)
+            step = lambda i: bsg.bs_gemv(bits[i % n], K, M, N, alpha[i % n], x[i % n],
+                                         colscale=csd[i % n] if cs else None, y=y[i % n])
+            emit("a1-a3,a7", "bs_gemv", name, _graph_us(step, steps, warmup), wb + 2 * N * B, K=K, B=B, colscale=cs)
+            del bits, alpha, csd, x, y
+            torch.cuda.empty_cache()
+
+    # a4, a5: the fused layer (bases + binary low-rank + protected int8 rows) and its parts
+    for name, M, N, K, r, frac in [("5120x5120 K=3 r=512", 5120, 5120, 3, 512, 0.0),
+                                   ("13824x5120 r=512 1% rows", 13824, 5120, 2, 512, 0.01),
+                                   ("5120x13824 r=512 1% rows", 5120, 13824, 2, 512, 0.01),
+                                   ("28672x8192 r=512 1% rows", 28672, 8192, 2, 512, 0.01)]:
+        ns = synth.n_salient(M, frac) if frac else 0
+        wb = K * M * N // 8 + 4 * K * M
+        lrb = r * N // 8 + M * r // 8 + 2 * r
+        sb = ns * N + 6 * ns
+        n = copies(wb + lrb + sb)
+        bits = rand_bits(K, M, N, n)
+        alpha = torch.rand((n, K, M), device=dev) * 0.02
+        U = rand_bits(1, M, r, n)
+        V = rand_bits(1, r, N, n)
+        ar = (torch.rand((n, r), device=dev) * 0.01).half().view(torch.int16)
+        rows = torch.stack([torch.sort(torch.randperm(M, device=dev)[:ns])[0] for _ in range(n)]).to(torch.int32) \
+            if ns else None
+        q = torch.randint(-127, 128, (n, ns, N), dtype=torch.int8, device=dev) if ns else None
+        sv = (torch.rand((n, ns), device=dev) * 1e-3).half().view(torch.int16) if ns else None
+        x = xs(N, 1, n)
+        y = torch.empty((n, M, 1), device=dev)
+        ws = bsg.new_workspace(bsg.lib().bsg_linear_workspace_bytes(r, 1), dev)
+
+        def step(i):
+            c = i % n
+            bsg.bsg_linear(bits[c], K, M, N, alpha[c], x[c], lowrank=(U[c], V[c], ar[c], r),
+                           salient=(rows[c], q[c], sv[c]) if ns else None, y=y[c], workspace=ws)
+        emit("a2-a5", "bsg_linear (2 launches)", name, _graph_us(step, steps, warmup), wb + lrb + sb + 2 * N,
+             K=K, r=r, ns=ns)
+        step = lambda i: bsg.binlr_apply(U[i % n], V[i % n], ar[i % n], r, M, N, x[i % n], y[i % n], workspace=ws)
+        emit("a4", "binlr_apply alone (2 launches)", name, _graph_us(step, steps, warmup), lrb + 2 * N, r=r)
+        if ns:
+            step = lambda i: bsg.salient_int8_apply(rows[i % n], q[i % n], sv[i % n], M, N, x[i % n], y[i % n])
+            emit("a5", "salient_int8_apply alone", name, _graph_us(step, steps, warmup), sb + 2 * N, ns=ns)
+        del bits, alpha, U, V, ar, rows, q, sv, x, y, ws
+        torch.cuda.empty_cache()
+
+    # a6: int8 activations, exact int32
+    for name, M, N, K in [("4096x4096", 4096, 4096, 2), ("gate/up 14336x4096", 14336, 4096, 2)]:
+        wb = K * M * N // 8 + 4 * K * M
+        n = copies(wb)
+        bits = rand_bits(K, M, N, n)
+        alpha = torch.rand((n, K, M), device=dev) * 0.02
+        xq = torch.randint(-127, 128, (n, N, 1), dtype=torch.int8, device=dev)
+        sx = torch.rand((n, 1), device=dev)
+        y = torch.empty((n, M, 1), device=dev)
+        step = lambda i: bsg.bs_gemv_i8(bits[i % n], K, M, N, alpha[i % n], xq[i % n], sx[i % n], want_acc=False,
+                                        y=y[i % n])
+        emit("a6", "bs_gemv_i8 (y)", name, _graph_us(step, steps, warmup), wb + N + 4, K=K)
+        xf = xs(N, 1, 2)
+        step = lambda i: bsg.bsq_quantize_i8(xf[i % 2])
+        emit("a6", "bsq_quantize_i8", "x of %d" % N, _graph_us(step, steps, warmup), 2 * N)
+        del bits, alpha, xq, sx, y, xf
+        torch.cuda.empty_cache()
+
+    # a0: packing (offline), eager
+    W = torch.randn((4096, 4096), device=dev) * 0.02
+    bsg.bsq_pack(W, 2, colscale=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        bsg.bsq_pack(W, 2, colscale=True)
+    torch.cuda.synchronize()
+    emit("a0", "bsq_pack (offline, eager)", "4096x4096 K=2 colscale", (time.perf_counter() - t0) / 5 * 1e6,
+         4096 * 4096 * 4, K=2)
+    return out
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -177,7 +313,12 @@ def main():
                     help="also run a plain %d MiB copy kernel (for scaling the traffic counters)" % (CALIB_BYTES >> 20))
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc output folders and exit")
+    ap.add_argument("--rows", action="store_true",
+                    help="time every row of the path on the pages' shapes (one JSON line per case) and exit")
     args = ap.parse_args()
+    if args.rows:
+        run_rows(min(args.steps, 200), min(args.warmup, 20))
+        return
     if args.pmc_summary:
         t = pmc_summary(*args.pmc_summary)
         with open(TRAFFIC_JSON, "w") as fh:

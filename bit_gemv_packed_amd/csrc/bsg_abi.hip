@@ -185,6 +185,7 @@ bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const float* alpha
   a.xdt = x_dtype;
   a.accumulate = accumulate ? 1 : 0;
   a.xvec = xvec_ok(x, colscale);
+  if (mfma_eligible(B, x_dtype, colscale != nullptr)) return hip_status(launch_prod_mfma(a, (hipStream_t)stream));
   return hip_status(launch_prod_f(a, p, (hipStream_t)stream));
 }
 

@@ -124,18 +124,18 @@ __device__ inline void fetch_act(const ProdArgs& a, const ActSrc& src, int n0, A
   }
 }
 
-// Tables of one chunk: the 16 signed sums of 4-column group `lane` (columns
+// Tables of one chunk: the 16 signed sums of 4-column group g (columns
 // n_lane .. n_lane + 3), for each of the KX column-scale sets and each batch
 // column: entry e = sum_j (2 bit_j(e) - 1) c_j x_j (FluxBin Sec. 3.2: the
 // column scale is folded in while the table is built).  Columns at or beyond
 // N give a zero table.
 template <int Q, int NWL, int KM, int BB, int XM>
-__device__ inline void build_tables(const ActSrc& s, const ActRaw<KM, BB>& act, int KX, int lane, int n_lane,
+__device__ inline void build_tables(const ActSrc& s, const ActRaw<KM, BB>& act, int KX, int g, int n_lane,
                                     char* lds, uint32_t wbase_lds) {
   constexpr int STEPS = NWL * 8;          // groups per lane quarter
   constexpr uint32_t ROWB = Q * 64 + 16;  // bytes of one step row: Q tables + 16 pad bytes
   constexpr uint32_t REG = STEPS * ROWB;  // bytes of one (base, batch column) table set
-  const int qq = lane / STEPS, ii = lane % STEPS;
+  const int qq = g / STEPS, ii = g % STEPS;
   const bool inb = n_lane < s.N;
 #pragma unroll
   for (int kx = 0; kx < KM; ++kx) {
@@ -247,7 +247,8 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
     k_prod_f(ProdArgs a) {
   constexpr int RW = 64 / Q;
   constexpr int CW = Q * NWL;
-  constexpr int G = CW * 8;  // 4-column groups per chunk (<= 64: one per lane)
+  constexpr int G = CW * 8;             // 4-column groups per chunk
+  constexpr int GPL = (G + 63) / 64;    // groups built per lane (lane, lane + 64)
   extern __shared__ __align__(16) char lds[];
 
   // every argument the prologue needs, in registers before anything else:
@@ -268,7 +269,8 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   const bool cs = a.colscale != nullptr;
   const int KX = cs ? a.K : 1;
   const uint32_t wbase_lds = (uint32_t)wv * a.wave_lds;
-  const bool builder = lane < G;  // this lane builds the tables of group `lane`
+  // lane builds the tables of groups lane + 64 i (i < GPL) that exist
+  auto grp = [&](int i) { return lane + 64 * i < G ? lane + 64 * i : 0; };
 
   float acc[KM][BB];
 #pragma unroll
@@ -284,10 +286,11 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   // three: a register copy between buffers would wait for the loads in
   // flight); activations stay one chunk ahead of the build.
   uint32_t wb0[KM][NWL], wb1[KM][NWL], wb2[KM][NWL];
-  ActRaw<KM, BB> act;
+  ActRaw<KM, BB> act[GPL];
   float al[KM];
   const int c0 = wv * a.NCH;  // this wavefront's first chunk
-  fetch_act<KM, BB, XM>(a, asrc, c0 * CW * 32 + (builder ? lane : 0) * 4, act);
+#pragma unroll
+  for (int i = 0; i < GPL; ++i) fetch_act<KM, BB, XM>(a, asrc, c0 * CW * 32 + grp(i) * 4, act[i]);
 #pragma unroll
   for (int k = 0; k < KM; ++k)
     if (base_active<KM>(a, k)) al[k] = __uint_as_float(ld32(alsrc, (uint32_t)(k * a.M + m) * 4u));
@@ -302,8 +305,14 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   // sign words two chunks ahead (into `ahead`), look up `cur`
   auto chunk = [&](int c, const uint32_t(&cur)[KM][NWL], uint32_t(&ahead)[KM][NWL]) {
     const int cw0 = (c0 + c) * CW;  // first word of the chunk
-    if (builder) build_tables<Q, NWL, KM, BB, XM>(asrc, act, KX, lane, cw0 * 32 + lane * 4, lds, wbase_lds);
-    fetch_act<KM, BB, XM>(a, asrc, (c0 + min(c + 1, clast)) * CW * 32 + (builder ? lane : 0) * 4, act);
+#pragma unroll
+    for (int i = 0; i < GPL; ++i)
+      if (lane + 64 * i < G)
+        build_tables<Q, NWL, KM, BB, XM>(asrc, act[i], KX, lane + 64 * i, cw0 * 32 + (lane + 64 * i) * 4, lds,
+                                         wbase_lds);
+#pragma unroll
+    for (int i = 0; i < GPL; ++i)
+      fetch_act<KM, BB, XM>(a, asrc, (c0 + min(c + 1, clast)) * CW * 32 + grp(i) * 4, act[i]);
     load_chunk<KM, NWL>(a, srows, (c0 + min(c + 2, clast)) * CW + q * NWL, ahead);
     wave_sync();  // the tables are private to this wavefront
     lookup_chunk<Q, NWL, KM, BB>(a, lds, wbase_lds, cs, q, cur, acc);
@@ -345,12 +354,17 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
 #pragma unroll
     for (int b = 0; b < BB; ++b) lacc[0][b] = 0.0f;
     for (int cu = wv; cu < tu; cu += a.W) {
-      ActRaw<1, BB> la;
+      ActRaw<1, BB> la[GPL];
       uint32_t uw[1][NWL];
-      fetch_act<1, BB, 0>(a, ls, cu * CW * 32 + (builder ? lane : 0) * 4, la);
+#pragma unroll
+      for (int i = 0; i < GPL; ++i) fetch_act<1, BB, 0>(a, ls, cu * CW * 32 + grp(i) * 4, la[i]);
       load_chunk<1, NWL>(a, urows, cu * CW + q * NWL, uw);
       wave_sync();  // earlier lookups of this wavefront's tables are done
-      if (builder) build_tables<Q, NWL, 1, BB, 0>(ls, la, 1, lane, cu * CW * 32 + lane * 4, lds, wbase_lds);
+#pragma unroll
+      for (int i = 0; i < GPL; ++i)
+        if (lane + 64 * i < G)
+          build_tables<Q, NWL, 1, BB, 0>(ls, la[i], 1, lane + 64 * i, cu * CW * 32 + (lane + 64 * i) * 4, lds,
+                                         wbase_lds);
       wave_sync();
       lookup_chunk<Q, NWL, 1, BB>(a, lds, wbase_lds, true, q, uw, lacc);
     }
@@ -454,9 +468,8 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8) {
   p.nlaunch = (B + p.BB - 1) / p.BB;
   // Lanes per row: the fewest that still give at least 256 workgroups
   // (one per compute unit) -- except for very tall matrices (>= 256 row
-  // blocks of 64), which run 2 lanes per row in 8-wavefront workgroups: four
-  // such workgroups fit a compute unit's LDS, so every workgroup is resident
-  // at once (measured fastest on 28672 x 8192).
+  // blocks of 64), which run 2 lanes per row (measured fastest on
+  // 28672 x 8192).
   const int forceQ = env_int("BSG_Q", 0);
   const bool tall = M >= 64 * 256;
   if (forceQ == 1 || forceQ == 2 || forceQ == 4) {
@@ -480,7 +493,7 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8) {
   p.NWL = p.CW / p.Q;
   p.wave_lds = i8 ? (size_t)p.CW * p.BB * 12 * 4 : (size_t)KX * p.BB * (p.NWL * 8) * (p.Q * 64 + 16);
   const int T = (ND + p.CW - 1) / p.CW;  // chunks
-  int W = env_int("BSG_WAVES", tall ? 8 : 16);
+  int W = env_int("BSG_WAVES", 16);
   const int wmax = prod_max_waves(p.KM, p.BB);
   W = W > wmax ? wmax : W;
   W = W > T ? T : W;

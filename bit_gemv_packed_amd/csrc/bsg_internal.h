@@ -105,6 +105,10 @@ struct ProdArgs {
 };
 
 hipError_t launch_prod_f(const ProdArgs& a, const ProdPlan& p, hipStream_t s);
+// Batched product on the matrix cores (bsg_gemv_mfma.hip): B >= 4 columns of
+// bf16 / fp16 x, no column scales.
+bool mfma_eligible(int B, int xdt, bool colscale);
+hipError_t launch_prod_mfma(const ProdArgs& a, hipStream_t s);
 hipError_t launch_prod_i8(const ProdArgs& a, const ProdPlan& p, hipStream_t s);
 
 }  // namespace bsg
