@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libbsg.so")
 
 BSG_F32, BSG_F16, BSG_BF16 = 0, 1, 2
 BSG_PACK_COLSCALE = 1
+BSG_ERR_HIP = -7
 
 _STATUS_NAMES = {0: "BSG_OK", -1: "BSG_ERR_NULL", -2: "BSG_ERR_SHAPE", -3: "BSG_ERR_DTYPE",
                  -4: "BSG_ERR_ALIGN", -5: "BSG_ERR_UNSUPPORTED", -6: "BSG_ERR_WORKSPACE", -7: "BSG_ERR_HIP"}
@@ -38,6 +39,8 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "bsg_abi_version": (ctypes.c_int32, []),
     "bsg_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+    "bsg_last_hip_error": (ctypes.c_int32, []),
+    "bsg_last_hip_error_string": (ctypes.c_char_p, []),
     "bsg_layout_words": (_SZ, [_I, _I, _I]),
     "bsg_layout_word_offset": (ctypes.c_int64, [_I, _I, _I, _I, _I, _I]),
     "bsg_binlr_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
@@ -82,7 +85,10 @@ def status_string(status: int) -> str:
 
 def _check(fn: str, status: int):
     if status != 0:
-        raise BsgError(fn, status, status_string(status))
+        msg = status_string(status)
+        if status == BSG_ERR_HIP:
+            msg += "; HIP error %d: %s" % (lib().bsg_last_hip_error(), lib().bsg_last_hip_error_string().decode())
+        raise BsgError(fn, status, msg)
 
 
 # ------------------------------------------------------------------ helpers

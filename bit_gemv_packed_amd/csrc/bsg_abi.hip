@@ -39,7 +39,13 @@ bool too_big(int K, int M, int N, int B) {
   return (size_t)K * M >= (1u << 30) || (size_t)N * B >= (1u << 30) || (size_t)K * N >= (1u << 30);
 }
 
-bsg_status hip_status(hipError_t e) { return e == hipSuccess ? BSG_OK : BSG_ERR_HIP; }
+thread_local hipError_t last_hip = hipSuccess;
+
+bsg_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return BSG_OK;
+  last_hip = e;
+  return BSG_ERR_HIP;
+}
 
 // binlr workspace: z, fp32 [r][B]
 size_t binlr_ws(int r, int B) { return align_up((size_t)r * B * 4, 256); }
@@ -53,6 +59,10 @@ bool xvec_ok(const void* x, const void* cs) {
 extern "C" {
 
 int32_t bsg_abi_version(void) { return kAbiVersion; }
+
+int32_t bsg_last_hip_error(void) { return (int32_t)last_hip; }
+
+const char* bsg_last_hip_error_string(void) { return hipGetErrorString(last_hip); }
 
 const char* bsg_status_string(bsg_status s) {
   switch (s) {

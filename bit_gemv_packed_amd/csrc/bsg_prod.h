@@ -4,7 +4,8 @@
 
 #include "bsg_internal.h"
 
-#include <atomic>
+#include <mutex>
+#include <unordered_set>
 
 namespace bsg {
 
@@ -65,6 +66,18 @@ struct SignRows {
   rsrc_t r[KM];
   uint32_t row_off;  // byte offset of this lane's row in a tile: (m % 64) * 16
 };
+// rb: the (uniform) 64-row block, m: this lane's row in it
+template <int KM>
+__device__ inline SignRows<KM> sign_rows_in(const uint32_t* bits, size_t plane, int K, int ND, int rb, int m) {
+  SignRows<KM> s;
+  const size_t blk = (size_t)64 * pad_words(ND);  // words of one row block
+  s.row_off = (uint32_t)(m & 63) * 16u;
+#pragma unroll
+  for (int k = 0; k < KM; ++k)
+    s.r[k] = make_rsrc(bits + (size_t)(k < K ? k : 0) * plane + (size_t)rb * blk, blk * 4);
+  return s;
+}
+// workgroup b owns rows [b RW, b RW + RW)
 template <int KM, int RW>
 __device__ inline SignRows<KM> sign_rows(const uint32_t* bits, size_t plane, int K, int ND, int m) {
   SignRows<KM> s;
@@ -137,13 +150,23 @@ __device__ inline T sum_waves(const T* p, int stride, int W) {
   return v[0];
 }
 
+// Workgroups of more than 32 KiB of LDS: the kernel's limit is raised once
+// per kernel (the set of raised kernels is shared by all threads).
+inline hipError_t allow_large_lds(const void* kern) {
+  static std::mutex mu;
+  static std::unordered_set<const void*> raised;
+  std::lock_guard<std::mutex> lock(mu);
+  if (raised.count(kern)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  if (e == hipSuccess) raised.insert(kern);
+  return e;
+}
+
 template <typename Kern>
 inline hipError_t launch_one(Kern kern, const ProdPlan& p, const ProdArgs& a, hipStream_t st) {
-  static std::atomic<int> raised{0};
-  if (p.lds > 65536 && !raised.load(std::memory_order_relaxed)) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  if (p.lds > 32768) {
+    const hipError_t e = allow_large_lds((const void*)kern);
     if (e != hipSuccess) return e;
-    raised.store(1, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL(kern, dim3(p.nwg), dim3(64 * p.W), p.lds, st, a);
   return hipGetLastError();

@@ -92,6 +92,11 @@ BSG_API int32_t bsg_abi_version(void);
 /* Static, NUL-terminated description of a status code. */
 BSG_API const char* bsg_status_string(bsg_status status);
 
+/* The HIP error behind the last BSG_ERR_HIP returned on the calling host
+ * thread (hipSuccess = 0 if none yet), and its description. */
+BSG_API int32_t bsg_last_hip_error(void);
+BSG_API const char* bsg_last_hip_error_string(void);
+
 /* Number of uint32 words of a device sign buffer for K bases of an M x N
  * matrix (K * plane, see the layout above).  0 if a size is invalid. */
 BSG_API size_t bsg_layout_words(int K, int M, int N);
