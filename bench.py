@@ -231,6 +231,49 @@ def run_rows(steps, warmup):
             del bits, alpha, csd, x, y
             torch.cuda.empty_cache()
 
+    # f2: projections that share x in one launch, and a whole decoder layer
+    layer = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
+             ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336)]
+    for B in (1, 16):
+        K = 2
+        wbs = {nm: K * M * N // 8 + 4 * K * M for nm, M, N in layer}
+        n = copies(sum(wbs.values()))
+        W = {nm: (rand_bits(K, M, N, n), torch.rand((n, K, M), device=dev) * 0.02) for nm, M, N in layer}
+        Y = {nm: torch.empty((n, M, B), device=dev) for nm, M, N in layer}
+        xa, xo, xm = xs(4096, B, n), xs(4096, B, n), xs(14336, B, n)
+        xin = {"q": xa, "k": xa, "v": xa, "o": xo, "gate": xa, "up": xa, "down": xm}
+        dims = {nm: (M, N) for nm, M, N in layer}
+
+        def proj(nm, c):
+            return (W[nm][0][c], dims[nm][0], W[nm][1][c], None, Y[nm][c])
+
+        def fused(names, c):
+            bsg.bs_gemv_multi([proj(nm, c) for nm in names], K, dims[names[0]][1], xin[names[0]][c])
+
+        def single(nm, c):
+            bsg.bs_gemv(W[nm][0][c], K, dims[nm][0], dims[nm][1], W[nm][1][c], xin[nm][c], y=Y[nm][c])
+
+        for names, label in [(("q", "k", "v"), "q+k+v 6144x4096"), (("gate", "up"), "gate+up 28672x4096")]:
+            by = sum(wbs[nm] for nm in names) + 2 * 4096 * B
+            emit("f2", "bs_gemv_multi (1 launch)" if B == 1 else "bs_gemv_multi (a launch each at B >= 4)",
+                 label, _graph_us(lambda i: fused(names, i % n), steps, warmup), by, K=K, B=B)
+            emit("f2", "bs_gemv, one call per projection", label,
+                 _graph_us(lambda i: [single(nm, i % n) for nm in names], steps, warmup), by, K=K, B=B)
+
+        def layer_fused(i):
+            c = i % n
+            fused(("q", "k", "v"), c)
+            single("o", c)
+            fused(("gate", "up"), c)
+            single("down", c)
+        by = sum(wbs.values()) + 2 * B * (4096 * 4 + 14336)
+        emit("f2", "decoder layer, 4 calls (q+k+v, o, gate+up, down)", "LLaMA-3-8B layer",
+             _graph_us(layer_fused, steps, warmup), by, K=K, B=B)
+        emit("f2", "decoder layer, 7 bs_gemv calls", "LLaMA-3-8B layer",
+             _graph_us(lambda i: [single(nm, i % n) for nm, _, _ in layer], steps, warmup), by, K=K, B=B)
+        del W, Y, xa, xo, xm, xin
+        torch.cuda.empty_cache()
+
     # a4, a5: the fused layer (bases + binary low-rank + protected int8 rows) and its parts
     for name, M, N, K, r, frac in [("5120x5120 K=3 r=512", 5120, 5120, 3, 512, 0.0),
                                    ("13824x5120 r=512 1% rows", 13824, 5120, 2, 512, 0.01),

@@ -55,6 +55,7 @@ _SIGS = {
     "bsg_layout_to_logical": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P]),
     "bs_gemv": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P]),
     "bs_gemv_i8": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _I, _P]),
+    "bs_gemv_multi": (ctypes.c_int32, [_P, _I, _I, _I, _P, _I, _I, _I, _P]),
     "binlr_apply": (ctypes.c_int32, [_P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P, _SZ, _P]),
     "salient_int8_apply": (ctypes.c_int32, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _P]),
     "bsg_linear_workspace_bytes": (_SZ, [_I, _I]),
@@ -270,6 +271,30 @@ def bs_gemv(bits, K: int, M: int, N: int, alpha, x, colscale=None, y=None, accum
     _check("bs_gemv", lib().bs_gemv(_ptr(bits), K, M, N, _ptr(alpha), _ptr(colscale), _ptr(x), _dtype_code(x), B,
                                     _ptr(y), 1 if accumulate else 0, _stream(dev)))
     return y
+
+
+class BsgProj(ctypes.Structure):
+    """Mirror of bsg_proj (include/bsg.h)."""
+    _fields_ = [("bits", ctypes.c_void_p), ("alpha", ctypes.c_void_p), ("colscale", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("M", ctypes.c_int)]
+
+
+def bs_gemv_multi(projs, K: int, N: int, x, accumulate: bool = False):
+    """Several bs_gemv products sharing x in one launch.  projs: list of (bits, M, alpha, colscale or None,
+    y or None); returns the list of y (fp32 [M][B])."""
+    torch = _torch()
+    B = _xshape(x, N)
+    dev = x.device
+    arr = (BsgProj * max(1, len(projs)))()
+    ys = []
+    for i, (bits, M, alpha, cs, y) in enumerate(projs):
+        if y is None:
+            y = torch.empty((M, B), dtype=torch.float32, device=dev)
+        ys.append(y)
+        arr[i] = BsgProj(_ptr(bits), _ptr(alpha), _ptr(cs), _ptr(y), M)
+    _check("bs_gemv_multi", lib().bs_gemv_multi(ctypes.cast(arr, ctypes.c_void_p), len(projs), K, N, _ptr(x),
+                                                _dtype_code(x), B, 1 if accumulate else 0, _stream(dev)))
+    return ys
 
 
 def bs_gemv_i8(bits, K: int, M: int, N: int, alpha, xq, sx, want_acc: bool = True, want_y: bool = True,

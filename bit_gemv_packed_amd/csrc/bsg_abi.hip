@@ -199,6 +199,61 @@ bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const float* alpha
   return hip_status(launch_prod_f(a, p, (hipStream_t)stream));
 }
 
+bsg_status bs_gemv_multi(const bsg_proj* projs, int P, int K, int N, const void* x, int x_dtype, int B,
+                         int accumulate, void* stream) {
+  if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
+  if (!projs) return BSG_ERR_NULL;
+  if (P < 1 || P > kMaxProj || K < 1 || K > kMaxK || bad_n(N) || B < 1 || B > kMaxB) return BSG_ERR_SHAPE;
+  const bool cs = projs[0].colscale != nullptr;
+  for (int i = 0; i < P; ++i) {
+    const bsg_proj& d = projs[i];
+    if (d.M < 0 || too_big(K, d.M, N, B) || (d.colscale != nullptr) != cs) return BSG_ERR_SHAPE;
+  }
+  if (!x) return BSG_ERR_NULL;
+  if (misaligned(x, dtype_size(x_dtype))) return BSG_ERR_ALIGN;
+  for (int i = 0; i < P; ++i) {
+    const bsg_proj& d = projs[i];
+    if (d.M == 0) continue;
+    if (!d.bits || !d.alpha || !d.y) return BSG_ERR_NULL;
+    if (misaligned(d.bits, 16) || misaligned(d.alpha, 4) || misaligned(d.colscale, 2) || misaligned(d.y, 4))
+      return BSG_ERR_ALIGN;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  ProdArgs a{};
+  a.x = x;
+  a.K = K;
+  a.N = N;
+  a.ND = N / 32;
+  a.B = B;
+  a.xdt = x_dtype;
+  a.accumulate = accumulate ? 1 : 0;
+  a.xvec = (((uintptr_t)x) % 16) == 0;
+  int np = 0;
+  for (int i = 0; i < P; ++i) {
+    const bsg_proj& d = projs[i];
+    if (d.M == 0) continue;
+    ProjDesc& e = a.proj[np++];
+    e.bits = d.bits;
+    e.alpha = d.alpha;
+    e.colscale = d.colscale;
+    e.y = d.y;
+    e.M = d.M;
+    if ((((uintptr_t)d.colscale) % 8) != 0) a.xvec = 0;
+  }
+  if (np == 0) return BSG_OK;
+  // one projection, or several batch columns: a launch each
+  if (np == 1 || B != 1) {
+    for (int i = 0; i < np; ++i) {
+      const ProjDesc& e = a.proj[i];
+      const bsg_status s = bs_gemv(e.bits, K, e.M, N, e.alpha, e.colscale, x, x_dtype, B, e.y, accumulate, stream);
+      if (s != BSG_OK) return s;
+    }
+    return BSG_OK;
+  }
+  a.np = np;
+  return hip_status(launch_prod_multi(a, st));
+}
+
 bsg_status bs_gemv_i8(const uint32_t* bits, int K, int M, int N, const float* alpha, const int8_t* xq,
                       const float* sx, int B, int32_t* acc, float* y, int accumulate, void* stream) {
   if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || N > (1 << 24) || B < 1 || B > kMaxB || too_big(K, M, N, B))

@@ -36,7 +36,7 @@ namespace bsg {
 // A float at an LDS byte address (the address already includes the base of
 // the dynamic LDS block), read with the address in one VGPR.
 typedef __attribute__((address_space(3))) const float lds_cf32;
-__device__ inline float lds_f32(uint32_t addr) { return *(lds_cf32*)(uintptr_t)addr; }
+__device__ __forceinline__ float lds_f32(uint32_t addr) { return *(lds_cf32*)(uintptr_t)addr; }
 
 // The activations one sign product multiplies: resources of x [N][B] and
 // of the column scales (size 0 when absent: their loads then read 0), and
@@ -48,7 +48,7 @@ struct ActSrc {
   int N, B, b0, xdt;
   bool cs;
 };
-__device__ inline ActSrc act_src(const ProdArgs& a) {
+__device__ __forceinline__ ActSrc act_src(const ProdArgs& a) {
   ActSrc s;
   s.x = make_rsrc(a.x, a.x_bytes);
   s.c = make_rsrc(a.colscale, a.cs_bytes);
@@ -59,7 +59,7 @@ __device__ inline ActSrc act_src(const ProdArgs& a) {
   s.cs = a.colscale != nullptr;
   return s;
 }
-__device__ inline ActSrc lr_src(const ProdArgs& a) {
+__device__ __forceinline__ ActSrc lr_src(const ProdArgs& a) {
   ActSrc s;
   s.x = make_rsrc(a.lr_z, (size_t)a.lr_r * a.B * 4);
   s.c = make_rsrc(a.lr_scale, (size_t)a.lr_r * 2);
@@ -72,7 +72,7 @@ __device__ inline ActSrc lr_src(const ProdArgs& a) {
 }
 
 // Raw activation bits -> fp32 (fp32 bits, or a bf16 / fp16 pattern in the low half).
-__device__ inline float decode_x(uint32_t raw, int xdt) {
+__device__ __forceinline__ float decode_x(uint32_t raw, int xdt) {
   const float h = f16_bits_to_float((uint16_t)raw);
   return xdt == BSG_F32 ? __uint_as_float(raw) : xdt == BSG_BF16 ? __uint_as_float(raw << 16) : h;
 }
@@ -93,7 +93,7 @@ struct ActRaw {
 // an fp32 element, unused otherwise), 16-bit loads of the scales.  Columns at
 // or beyond N read 0.
 template <int KM, int BB, int XM>
-__device__ inline void fetch_act(const ProdArgs& a, const ActSrc& src, int n0, ActRaw<KM, BB>& r) {
+__device__ __forceinline__ void fetch_act(const ProdArgs& a, const ActSrc& src, int n0, ActRaw<KM, BB>& r) {
   if (XM != 0) {
     const uint2 v = ld64(src.x, (uint32_t)n0 * 2u);
     r.x[0][0] = v.x;
@@ -130,7 +130,7 @@ __device__ inline void fetch_act(const ProdArgs& a, const ActSrc& src, int n0, A
 // column scale is folded in while the table is built).  Columns at or beyond
 // N give a zero table.
 template <int Q, int NWL, int KM, int BB, int XM>
-__device__ inline void build_tables(const ActSrc& s, const ActRaw<KM, BB>& act, int KX, int g, int n_lane,
+__device__ __forceinline__ void build_tables(const ActSrc& s, const ActRaw<KM, BB>& act, int KX, int g, int n_lane,
                                     char* lds, uint32_t wbase_lds) {
   constexpr int STEPS = NWL * 8;          // groups per lane quarter
   constexpr uint32_t ROWB = Q * 64 + 16;  // bytes of one step row: Q tables + 16 pad bytes
@@ -176,7 +176,7 @@ __device__ inline void build_tables(const ActSrc& s, const ActRaw<KM, BB>& act, 
 // of every base is looked up together: 8K independent LDS reads in flight
 // and K independent add chains.
 template <int Q, int NWL, int KM, int BB>
-__device__ inline void lookup_chunk(const ProdArgs& a, const char* lds, uint32_t wbase_lds, bool cs, int q,
+__device__ __forceinline__ void lookup_chunk(const ProdArgs& a, const char* lds, uint32_t wbase_lds, bool cs, int q,
                                     const uint32_t (&cur)[KM][NWL], float (&acc)[KM][BB]) {
   constexpr uint32_t ROWB = Q * 64 + 16;             // bytes of one step row of tables
   constexpr uint32_t REG = NWL * 8 * ROWB;           // bytes of one (base, batch column) table set
@@ -221,7 +221,7 @@ __device__ inline void lookup_chunk(const ProdArgs& a, const char* lds, uint32_t
 // First index i in [0, n) with rows[i] >= key (n if none), rows ascending:
 // a 64-way search, one probe per lane per round, so about log64(n) + 1
 // dependent loads.  Uniform over the wavefront.
-__device__ inline int lower_bound_rows(rsrc_t rows, int n, int key, int lane) {
+__device__ __forceinline__ int lower_bound_rows(rsrc_t rows, int n, int key, int lane) {
   int lo = 0, hi = n;
   while (lo < hi) {
     const int step = (hi - lo + 63) / 64;
@@ -237,13 +237,16 @@ __device__ inline int lower_bound_rows(rsrc_t rows, int n, int key, int lane) {
   return lo;
 }
 
-// Register budget.  With one or two bases, one batch column and Q >= 2 the
-// tables of a 16-wavefront workgroup take at most half the LDS, and the
-// kernel is held to 64 VGPRs (8 wavefronts per SIMD) so that two such
-// workgroups share a compute unit.  Instances with KM * BB >= 8 keep more
+// Register budget.  With one or two bases, one aligned 16-bit batch column
+// and Q >= 2 the tables of a 16-wavefront workgroup take at most half the
+// LDS, and the kernel is held to 64 VGPRs (8 wavefronts per SIMD) so that two
+// such workgroups share a compute unit (the generic activation path needs
+// more registers and is not held).  Instances with KM * BB >= 8 keep more
 // sums in registers and run at most 8 wavefronts per workgroup.
-template <int Q, int NWL, int KM, int BB, int XM>
-__global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB == 1 && Q >= 2) ? 8 : 1)
+// MP = 1: the fused launch of several projections (bs_gemv_multi); the
+// single-product instances (MP = 0) carry none of its code.
+template <int Q, int NWL, int KM, int BB, int XM, int MP>
+__global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB == 1 && Q >= 2 && XM != 0) ? 8 : 1)
     k_prod_f(ProdArgs a) {
   constexpr int RW = 64 / Q;
   constexpr int CW = Q * NWL;
@@ -256,14 +259,33 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   asm volatile("" ::"s"(a.bits), "s"(a.alpha), "s"(a.colscale), "s"(a.x), "s"(a.plane), "s"(a.K), "s"(a.M),
                "s"(a.N), "s"(a.ND), "s"(a.B), "s"(a.b0), "s"(a.xdt), "s"(a.NCH), "s"(a.wave_lds), "s"(a.x_bytes),
                "s"(a.cs_bytes), "s"(a.al_bytes));
+  // fused launch: this workgroup's projection and its block within it
+  int blk = blockIdx.x;
+  if (MP) {
+    // constant indices only (a computed index would copy the arguments to
+    // scratch memory)
+    ProjDesc d = a.proj[0];
+#pragma unroll
+    for (int i = 1; i < kMaxProj; ++i)
+      if (i < a.np && (int)blockIdx.x >= a.proj[i].wg0) d = a.proj[i];
+    a.bits = d.bits;
+    a.alpha = d.alpha;
+    a.colscale = d.colscale;
+    a.y = d.y;
+    a.plane = d.plane;
+    a.M = d.M;
+    a.al_bytes = d.al_bytes;
+    a.cs_bytes = d.cs_bytes;
+    blk = blockIdx.x - d.wg0;
+  }
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wavefront index (uniform)
   const int q = lane / RW;
   const int r = lane % RW;
-  const int m = blockIdx.x * RW + r;
+  const int m = blk * RW + r;
   const bool valid = m < a.M;
   // rows beyond M read padding; their sums are dropped
-  const SignRows<KM> srows = sign_rows<KM, RW>(a.bits, a.plane, a.K, a.ND, m);
+  const SignRows<KM> srows = sign_rows<KM, RW>(a.bits, a.plane, a.K, a.ND, blk, m);
   const ActSrc asrc = act_src(a);
   const rsrc_t alsrc = make_rsrc(a.alpha, a.al_bytes);
   const bool cs = a.colscale != nullptr;
@@ -348,7 +370,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   if (a.lr_bits) {
     const ActSrc ls = lr_src(a);
     const int ndu = a.lr_r / 32;
-    const SignRows<1> urows = sign_rows<1, RW>(a.lr_bits, a.lr_plane, 1, ndu, m);
+    const SignRows<1> urows = sign_rows<1, RW>(a.lr_bits, a.lr_plane, 1, ndu, blk, m);
     const int tu = (pad_words(ndu) + CW - 1) / CW;
     float lacc[1][BB];
 #pragma unroll
@@ -379,7 +401,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
     const rsrc_t rs = make_rsrc(a.sal_rows, (size_t)a.sal_n * 4);
     const rsrc_t qs = make_rsrc(a.sal_q, (size_t)a.sal_n * a.N);
     const rsrc_t ss = make_rsrc(a.sal_s, (size_t)a.sal_n * 2);
-    const int m0 = blockIdx.x * RW;
+    const int m0 = blk * RW;
     const int i0 = lower_bound_rows(rs, a.sal_n, m0, lane);
     const int i1 = lower_bound_rows(rs, a.sal_n, m0 + RW, lane);
     for (int i = i0 + wv; i < i1; i += a.W) {
@@ -442,7 +464,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   __syncthreads();
   for (int t = threadIdx.x; t < RW * BB; t += blockDim.x) {  // blockDim may be below RW * BB
     const int rr = t / BB, b = t % BB;
-    const int mm = blockIdx.x * RW + rr;
+    const int mm = blk * RW + rr;
     if (mm < a.M && a.b0 + b < a.B) {
       const float s = sum_waves(red + rr * BB + b, RW * BB, a.W);
       const size_t yi = (size_t)mm * a.B + a.b0 + b;
@@ -507,13 +529,51 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8) {
 }
 
 static hipError_t dispatch_f(const ProdArgs& a, const ProdPlan& p, hipStream_t st) {
+  if (a.np > 1) {
+    if (p.BB != 1) return hipErrorInvalidConfiguration;
+    switch (prod_key(p.Q, p.NWL, p.KM, p.BB, p.XM)) {
+#define BSG_CASE(Q, NWL, KM, BB, XM) \
+  case prod_key(Q, NWL, KM, BB, XM): return launch_one(k_prod_f<Q, NWL, KM, BB, XM, 1>, p, a, st);
+      BSG_PROD_F_ONE_COLUMN(BSG_CASE)
+#undef BSG_CASE
+      default: return hipErrorInvalidConfiguration;
+    }
+  }
   switch (prod_key(p.Q, p.NWL, p.KM, p.BB, p.XM)) {
 #define BSG_CASE(Q, NWL, KM, BB, XM) \
-  case prod_key(Q, NWL, KM, BB, XM): return launch_one(k_prod_f<Q, NWL, KM, BB, XM>, p, a, st);
+  case prod_key(Q, NWL, KM, BB, XM): return launch_one(k_prod_f<Q, NWL, KM, BB, XM, 0>, p, a, st);
     BSG_PROD_F_INSTANCES(BSG_CASE)
 #undef BSG_CASE
     default: return hipErrorInvalidConfiguration;
   }
+}
+
+// Fused launch over the projections a0.proj[0 .. a0.np) (same K, N, x and
+// column-scale presence; one batch column): one grid, the row blocks of each
+// projection in turn, planned for their total rows.
+hipError_t launch_prod_multi(const ProdArgs& a0, hipStream_t st) {
+  int mt = 0;
+  for (int i = 0; i < a0.np; ++i) mt += a0.proj[i].M;
+  ProdPlan p = plan_prod(a0.K, mt, a0.N, a0.B, a0.proj[0].colscale != nullptr, false);
+  ProdArgs a = a0;
+  int wg = 0;
+  for (int i = 0; i < a.np; ++i) {
+    ProjDesc& d = a.proj[i];
+    d.plane = plane_words(d.M, a.ND);
+    d.wg0 = wg;
+    d.al_bytes = (uint32_t)((size_t)a.K * d.M * 4);
+    d.cs_bytes = d.colscale ? (uint32_t)((size_t)a.K * a.N * 2) : 0u;
+    wg += (d.M + p.RW - 1) / p.RW;
+  }
+  p.nwg = wg;
+  // the kernel prologue reads these before it switches to its projection
+  a.bits = a.proj[0].bits;
+  a.alpha = a.proj[0].alpha;
+  a.colscale = a.proj[0].colscale;
+  a.y = a.proj[0].y;
+  a.plane = a.proj[0].plane;
+  a.M = a.proj[0].M;
+  return launch_prod_f(a, p, st);
 }
 
 hipError_t launch_prod_f(const ProdArgs& a0, const ProdPlan& p0, hipStream_t st) {

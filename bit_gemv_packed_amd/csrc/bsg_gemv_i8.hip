@@ -29,7 +29,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB)) k_prod_i8(ProdArg
   const int m = blockIdx.x * RW + r;
   const bool valid = m < a.M;
   // rows beyond M read padding; their sums are dropped
-  const SignRows<KM> srows = sign_rows<KM, RW>(a.bits, a.plane, a.K, a.ND, m);
+  const SignRows<KM> srows = sign_rows<KM, RW>(a.bits, a.plane, a.K, a.ND, blockIdx.x, m);
   const rsrc_t xsrc = make_rsrc(a.xq, (size_t)a.N * a.B);
   uint32_t* pl = (uint32_t*)(lds + (size_t)wv * a.wave_lds);
 

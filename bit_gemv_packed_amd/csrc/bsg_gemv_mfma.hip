@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(64 * mfma_max_waves(RT, KM, VW)) k_prod_mfma(P
 
   SignRows<KM> sr[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) sr[rt] = sign_rows<KM, 16 * RT>(a.bits, a.plane, a.K, a.ND, m0 + rt * 16 + r16);
+  for (int rt = 0; rt < RT; ++rt) sr[rt] = sign_rows<KM, 16 * RT>(a.bits, a.plane, a.K, a.ND, blockIdx.x, m0 + rt * 16 + r16);
   const rsrc_t xs = make_rsrc(a.x, a.x_bytes);
 
   f32x4 acc[RT][KM];

@@ -69,6 +69,19 @@ struct ProdPlan {
 
 ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool int8_mode);
 
+// One projection of a fused launch (bs_gemv_multi): its own weights, scales
+// and output, the first workgroup of its row blocks in the grid.
+constexpr int kMaxProj = 8;
+struct ProjDesc {
+  const uint32_t* bits;
+  const float* alpha;
+  const uint16_t* colscale;
+  float* y;
+  size_t plane;
+  int M, wg0;
+  uint32_t al_bytes, cs_bytes;
+};
+
 struct ProdArgs {
   // Read by the prologue of every product kernel: kept together at the front
   // so that they arrive in one batch of scalar loads.
@@ -102,9 +115,15 @@ struct ProdArgs {
   const int32_t* sal_rows;   // [sal_n], ascending
   const int8_t* sal_q;       // [sal_n][N]
   const uint16_t* sal_s;     // fp16 [sal_n]
+  // Fused launch of np > 1 projections sharing x (float path, bases only):
+  // workgroup w works for the last projection p with proj[p].wg0 <= w.
+  int np;
+  ProjDesc proj[kMaxProj];
 };
 
 hipError_t launch_prod_f(const ProdArgs& a, const ProdPlan& p, hipStream_t s);
+// One launch over a.np > 1 projections (a.proj) sharing x (bsg_gemv.hip).
+hipError_t launch_prod_multi(const ProdArgs& a, hipStream_t s);
 // Batched product on the matrix cores (bsg_gemv_mfma.hip): B >= 4 columns of
 // bf16 / fp16 x, no column scales.
 bool mfma_eligible(int B, int xdt, bool colscale);

@@ -77,17 +77,10 @@ __device__ inline SignRows<KM> sign_rows_in(const uint32_t* bits, size_t plane, 
     s.r[k] = make_rsrc(bits + (size_t)(k < K ? k : 0) * plane + (size_t)rb * blk, blk * 4);
   return s;
 }
-// workgroup b owns rows [b RW, b RW + RW)
+// workgroup blk (uniform) owns rows [blk RW, blk RW + RW)
 template <int KM, int RW>
-__device__ inline SignRows<KM> sign_rows(const uint32_t* bits, size_t plane, int K, int ND, int m) {
-  SignRows<KM> s;
-  const int rb = (int)(blockIdx.x * RW) >> 6;
-  const size_t blk = (size_t)64 * pad_words(ND);  // words of one row block
-  s.row_off = (uint32_t)(m & 63) * 16u;
-#pragma unroll
-  for (int k = 0; k < KM; ++k)
-    s.r[k] = make_rsrc(bits + (size_t)(k < K ? k : 0) * plane + (size_t)rb * blk, blk * 4);
-  return s;
+__device__ inline SignRows<KM> sign_rows(const uint32_t* bits, size_t plane, int K, int ND, int blk, int m) {
+  return sign_rows_in<KM>(bits, plane, K, ND, (blk * RW) >> 6, m);
 }
 
 // Sign words of one chunk: NWL consecutive logical words [w0, w0 + NWL) of
@@ -177,12 +170,12 @@ inline hipError_t launch_one(Kern kern, const ProdPlan& p, const ProdArgs& a, hi
 // bf16 / fp16 single-column activation path of the float kernel.  Several
 // batch columns: 4-word chunks, generic activation path.
 #define BSG_PROD_XM(X, Q, NWL, KM) X(Q, NWL, KM, 1, 0) X(Q, NWL, KM, 1, 1) X(Q, NWL, KM, 1, 2)
-#define BSG_PROD_F_INSTANCES(X)                                                                              \
+#define BSG_PROD_F_ONE_COLUMN(X)                                                                             \
   BSG_PROD_XM(X, 4, 2, 1) BSG_PROD_XM(X, 4, 2, 2) BSG_PROD_XM(X, 2, 4, 1) BSG_PROD_XM(X, 2, 4, 2)            \
   BSG_PROD_XM(X, 1, 8, 1) BSG_PROD_XM(X, 1, 8, 2) BSG_PROD_XM(X, 4, 1, 3) BSG_PROD_XM(X, 4, 1, 4)            \
   BSG_PROD_XM(X, 4, 1, 8) BSG_PROD_XM(X, 2, 2, 3) BSG_PROD_XM(X, 2, 2, 4) BSG_PROD_XM(X, 2, 2, 8)            \
-  BSG_PROD_XM(X, 1, 4, 3) BSG_PROD_XM(X, 1, 4, 4) BSG_PROD_XM(X, 1, 4, 8) BSG_PROD_MULTI_B(X, 2)             \
-  BSG_PROD_I8_MULTI_B(X, 4)
+  BSG_PROD_XM(X, 1, 4, 3) BSG_PROD_XM(X, 1, 4, 4) BSG_PROD_XM(X, 1, 4, 8)
+#define BSG_PROD_F_INSTANCES(X) BSG_PROD_F_ONE_COLUMN(X) BSG_PROD_MULTI_B(X, 2) BSG_PROD_I8_MULTI_B(X, 4)
 #define BSG_PROD_I8_INSTANCES(X)                                                                       \
   X(4, 2, 1, 1, 0) X(4, 2, 2, 1, 0) X(2, 4, 1, 1, 0) X(2, 4, 2, 1, 0) X(1, 8, 1, 1, 0) X(1, 8, 2, 1, 0) \
   X(4, 1, 3, 1, 0) X(4, 1, 4, 1, 0) X(4, 1, 8, 1, 0) X(2, 2, 3, 1, 0) X(2, 2, 4, 1, 0) X(2, 2, 8, 1, 0) \

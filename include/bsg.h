@@ -218,6 +218,32 @@ BSG_API bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const floa
                    float* y, int accumulate, void* stream);
 
 /*
+ * bs_gemv_multi -- several bs_gemv products that share x, in one launch
+ * (projections that read the same activations, e.g. the query, key and
+ * value projections, or the two projections of a gated MLP):
+ *   for each i < P:  projs[i].y (= or +=) bs_gemv term of projs[i]
+ *   projs     (host) P descriptors, read during the call only:
+ *             bits (device layout, K bases of M x N), alpha fp32 [K][M],
+ *             colscale fp16 [K][N] or NULL, y fp32 [M][B], M (>= 0)
+ *   x         (device) [N][B] of dtype x_dtype, shared by all projections
+ * 1 <= P <= 8; K, N, B, x and accumulate are common; colscale must be given
+ * for every projection or for none (BSG_ERR_SHAPE otherwise).  Each y is
+ * what bs_gemv would write, within the same bound (the fused plan may sum in
+ * another order).  The grid holds the row blocks of every projection in
+ * turn, so small projections share one launch and its latency.  With B > 1
+ * batch columns the projections are launched one after another.
+ */
+typedef struct bsg_proj {
+  const uint32_t* bits;
+  const float* alpha;
+  const uint16_t* colscale;
+  float* y;
+  int M;
+} bsg_proj;
+BSG_API bsg_status bs_gemv_multi(const bsg_proj* projs, int P, int K, int N, const void* x, int x_dtype, int B,
+                                 int accumulate, void* stream);
+
+/*
  * bs_gemv_i8 -- the same product with int8 activations, exact in integers:
  *   acc[k][m][b] = sum_n (2 bit_k(m,n) - 1) * xq[n,b]            (int32, exact)
  *   y[m,b] (= or +=) sx[b] * sum_k alpha[k][m] * acc[k][m][b]    (fp32)

@@ -112,6 +112,38 @@ def test_bs_gemv_validation():
     assert _gemv(y=A16d + 2) == EALIGN
 
 
+def _multi(projs, K=2, N=256, x=A16c, dt=2, B=1, acc=0, P=None):
+    arr = (bsg.BsgProj * max(1, len(projs)))(*[bsg.BsgProj(*p) for p in projs])
+    return bsg.lib().bs_gemv_multi(ctypes.cast(arr, ctypes.c_void_p), len(projs) if P is None else P, K, N, x, dt, B,
+                                   acc, None)
+
+
+@fake_ptrs
+def test_bs_gemv_multi_validation():
+    q = (A16, A16b, None, A16d, 128)
+    assert _multi([q], dt=7) == EDTYPE
+    assert bsg.lib().bs_gemv_multi(None, 1, 2, 256, A16c, 2, 1, 0, None) == ENULL
+    assert _multi([q], P=0) == ESHAPE
+    assert _multi([q] * 9) == ESHAPE                # at most 8 projections
+    assert _multi([q], K=0) == ESHAPE
+    assert _multi([q], K=9) == ESHAPE
+    assert _multi([q], N=33) == ESHAPE
+    assert _multi([q], B=0) == ESHAPE
+    assert _multi([q], B=65) == ESHAPE
+    assert _multi([q, (A16, A16b, None, A16d, -1)]) == ESHAPE
+    assert _multi([q, (A16, A16b, A16c, A16d, 64)]) == ESHAPE   # column scales for some projections only
+    assert _multi([q], x=None) == ENULL
+    assert _multi([q], x=A16c + 1) == EALIGN
+    assert _multi([q, (None, A16b, None, A16d, 64)]) == ENULL
+    assert _multi([q, (A16, None, None, A16d, 64)]) == ENULL
+    assert _multi([q, (A16, A16b, None, None, 64)]) == ENULL
+    assert _multi([q, (A16 + 4, A16b, None, A16d, 64)]) == EALIGN
+    assert _multi([q, (A16, A16b + 2, None, A16d, 64)]) == EALIGN
+    assert _multi([q, (A16, A16b, None, A16d + 2, 64)]) == EALIGN
+    assert _multi([(A16, A16b, A16c, A16d, 64), (A16, A16b, A16c + 1, A16d, 64)]) == EALIGN
+    assert _multi([(None, None, None, None, 0)]) == OK   # empty outputs: a no-op
+
+
 @fake_ptrs
 def test_bs_gemv_i8_validation():
     L = bsg.lib()
