@@ -255,7 +255,7 @@ def run_rows(steps, warmup):
 
         for names, label in [(("q", "k", "v"), "q+k+v 6144x4096"), (("gate", "up"), "gate+up 28672x4096")]:
             by = sum(wbs[nm] for nm in names) + 2 * 4096 * B
-            emit("f2", "bs_gemv_multi (1 launch)" if B == 1 else "bs_gemv_multi (a launch each at B >= 4)",
+            emit("f2", "bs_gemv_multi (1 launch)" if B == 1 else "bs_gemv_multi (1 launch, matrix cores)",
                  label, _graph_us(lambda i: fused(names, i % n), steps, warmup), by, K=K, B=B)
             emit("f2", "bs_gemv, one call per projection", label,
                  _graph_us(lambda i: [single(nm, i % n) for nm in names], steps, warmup), by, K=K, B=B)

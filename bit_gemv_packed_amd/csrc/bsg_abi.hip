@@ -241,7 +241,14 @@ bsg_status bs_gemv_multi(const bsg_proj* projs, int P, int K, int N, const void*
     if ((((uintptr_t)d.colscale) % 8) != 0) a.xvec = 0;
   }
   if (np == 0) return BSG_OK;
-  // one projection, or several batch columns: a launch each
+  // several batch columns on the matrix cores: one fused launch per 16
+  // columns (and 4 bases)
+  if (np > 1 && mfma_eligible(B, x_dtype, cs) && mfma_multi_ok(B, x)) {
+    a.np = np;
+    return hip_status(launch_prod_mfma(a, st));
+  }
+  // one projection, or several batch columns off the matrix cores: a launch
+  // each
   if (np == 1 || B != 1) {
     for (int i = 0; i < np; ++i) {
       const ProjDesc& e = a.proj[i];

@@ -98,24 +98,41 @@ struct MfTile {
 };
 
 // XT: 1 bf16, 2 fp16 activations.  VW: batch values per x load (8, 4, 2 or
-// 1: B % VW == 0 and x aligned to 2 VW bytes).
-template <int RT, int KM, int XT, int VW>
+// 1: B % VW == 0 and x aligned to 2 VW bytes).  MP = 1: the fused launch of
+// several projections (bs_gemv_multi).
+template <int RT, int KM, int XT, int VW, int MP>
 __global__ void __launch_bounds__(64 * mfma_max_waves(RT, KM, VW)) k_prod_mfma(ProdArgs a) {
   asm volatile("" ::"s"(a.bits), "s"(a.alpha), "s"(a.x), "s"(a.y), "s"(a.plane), "s"(a.K), "s"(a.M), "s"(a.N),
                "s"(a.ND), "s"(a.B), "s"(a.b0), "s"(a.accumulate), "s"(a.NCH), "s"(a.x_bytes), "s"(a.al_bytes));
+  // fused launch: this workgroup's projection (constant indices only: a
+  // computed index would copy the arguments to scratch memory)
+  int blk = blockIdx.x;
+  if (MP) {
+    ProjDesc d = a.proj[0];
+#pragma unroll
+    for (int i = 1; i < kMaxProj; ++i)
+      if (i < a.np && (int)blockIdx.x >= a.proj[i].wg0) d = a.proj[i];
+    a.bits = d.bits;
+    a.alpha = d.alpha;
+    a.y = d.y;
+    a.plane = d.plane;
+    a.M = d.M;
+    a.al_bytes = d.al_bytes;
+    blk = blockIdx.x - d.wg0;
+  }
   extern __shared__ __align__(16) char lds[];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int m0 = blockIdx.x * 16 * RT;
+  const int m0 = blk * 16 * RT;
   const uint32_t xt = (uint32_t)(uintptr_t)lds + (uint32_t)wv * kXtBytes;
   uint32_t msk;
   asm volatile("s_mov_b32 %0, 0x80008000" : "=s"(msk));
 
   SignRows<KM> sr[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) sr[rt] = sign_rows<KM, 16 * RT>(a.bits, a.plane, a.K, a.ND, blockIdx.x, m0 + rt * 16 + r16);
+  for (int rt = 0; rt < RT; ++rt) sr[rt] = sign_rows<KM, 16 * RT>(a.bits, a.plane, a.K, a.ND, blk, m0 + rt * 16 + r16);
   const rsrc_t xs = make_rsrc(a.x, a.x_bytes);
 
   f32x4 acc[RT][KM];
@@ -247,9 +264,23 @@ static hipError_t dispatch_mfma(const ProdArgs& a, int RT, int KM, int XT, int V
   p.nwg = nwg;
   p.W = W;
   p.lds = lds;
+  if (a.np > 1) {
+    switch (key) {
+#define BSG_MF(RT_, KM_, XT_, VW_) \
+  case ((RT_ * 8 + KM_) * 4 + XT_) * 16 + VW_: return launch_one(k_prod_mfma<RT_, KM_, XT_, VW_, 1>, p, a, st);
+#define BSG_MF_VW(RT_, KM_, XT_) BSG_MF(RT_, KM_, XT_, 4) BSG_MF(RT_, KM_, XT_, 8)
+#define BSG_MF_XT(RT_, KM_) BSG_MF_VW(RT_, KM_, 1) BSG_MF_VW(RT_, KM_, 2)
+      BSG_MF_XT(1, 1) BSG_MF_XT(1, 2) BSG_MF_XT(1, 3) BSG_MF_XT(1, 4)
+      BSG_MF_XT(2, 1) BSG_MF_XT(2, 2) BSG_MF_XT(2, 3) BSG_MF_XT(2, 4)
+#undef BSG_MF_XT
+#undef BSG_MF_VW
+#undef BSG_MF
+      default: return hipErrorInvalidConfiguration;
+    }
+  }
   switch (key) {
 #define BSG_MF(RT_, KM_, XT_, VW_) \
-  case ((RT_ * 8 + KM_) * 4 + XT_) * 16 + VW_: return launch_one(k_prod_mfma<RT_, KM_, XT_, VW_>, p, a, st);
+  case ((RT_ * 8 + KM_) * 4 + XT_) * 16 + VW_: return launch_one(k_prod_mfma<RT_, KM_, XT_, VW_, 0>, p, a, st);
 #define BSG_MF_VW(RT_, KM_, XT_) BSG_MF(RT_, KM_, XT_, 2) BSG_MF(RT_, KM_, XT_, 4) BSG_MF(RT_, KM_, XT_, 8)
 #define BSG_MF_XT(RT_, KM_) BSG_MF_VW(RT_, KM_, 1) BSG_MF_VW(RT_, KM_, 2)
     BSG_MF_XT(1, 1) BSG_MF_XT(1, 2) BSG_MF_XT(1, 3) BSG_MF_XT(1, 4)
@@ -271,20 +302,38 @@ static int mf_env(const char* name, int dflt) {
   return r > 0 ? r : dflt;
 }
 
+// x load width for this batch width and x address
+static int mfma_vw(int B, const void* x) {
+  const uintptr_t xa = (uintptr_t)x;
+  return (B % 8 == 0 && xa % 16 == 0) ? 8 : (B % 4 == 0 && xa % 8 == 0) ? 4 : (B % 2 == 0 && xa % 4 == 0) ? 2 : 1;
+}
+
+bool mfma_multi_ok(int B, const void* x) { return mfma_vw(B, x) >= 4; }
+
 // One launch per 16 batch columns and per group of up to 4 bases (2 with
 // 2-byte x loads; later groups accumulate).  Row tiles per workgroup: 2 when
 // that still gives at least 256 workgroups (x is then read once per 32
 // rows), else 1.  Wavefronts: up to mfma_max_waves, each taking whole
-// 4-step layout tiles.
+// 4-step layout tiles.  With a0.np > 1 every launch covers the row tiles of
+// all projections a0.proj[0 .. np) in turn (4- or 8-value x loads only).
 hipError_t launch_prod_mfma(const ProdArgs& a0, hipStream_t st) {
   const int T4 = (a0.ND + 3) / 4;      // 4-step layout tiles
   const int XT = a0.xdt == BSG_BF16 ? 1 : 2;
-  const uintptr_t xa = (uintptr_t)a0.x;
-  const int VW = (a0.B % 8 == 0 && xa % 16 == 0) ? 8 : (a0.B % 4 == 0 && xa % 8 == 0) ? 4
-                 : (a0.B % 2 == 0 && xa % 4 == 0) ? 2 : 1;
-  const int RT = VW == 1 ? 1 : mf_env("BSG_MF_RT", (a0.M + 31) / 32 >= 256 ? 2 : 1) >= 2 ? 2 : 1;
+  const int VW = mfma_vw(a0.B, a0.x);
+  const bool multi = a0.np > 1;
+  if (multi && VW < 4) return hipErrorInvalidConfiguration;
+  int mt = a0.M;
+  if (multi) {
+    mt = 0;
+    for (int i = 0; i < a0.np; ++i) mt += a0.proj[i].M;
+  }
+  const int RT = VW == 1 ? 1 : mf_env("BSG_MF_RT", (mt + 31) / 32 >= 256 ? 2 : 1) >= 2 ? 2 : 1;
   const int KG = VW == 1 ? 2 : 4;      // bases per launch
-  const int nwg = (a0.M + 16 * RT - 1) / (16 * RT);
+  int nwg = (a0.M + 16 * RT - 1) / (16 * RT);
+  if (multi) {
+    nwg = 0;
+    for (int i = 0; i < a0.np; ++i) nwg += (a0.proj[i].M + 16 * RT - 1) / (16 * RT);
+  }
   for (int k0 = 0; k0 < a0.K; k0 += KG) {
     const int KM = a0.K - k0 < KG ? a0.K - k0 : KG;
     const int wmax = std::min(mfma_max_waves(RT, KM, VW), mf_env("BSG_MF_W", 16));
@@ -302,6 +351,19 @@ hipError_t launch_prod_mfma(const ProdArgs& a0, hipStream_t st) {
     as.al_bytes = a0.alpha ? (uint32_t)((size_t)KM * a0.M * 4) : 0u;
     as.W = W;
     as.NCH = per * 4;  // steps per wavefront
+    if (multi) {
+      int wg = 0;
+      for (int i = 0; i < a0.np; ++i) {
+        const ProjDesc& s0 = a0.proj[i];
+        ProjDesc& d = as.proj[i];
+        d.plane = plane_words(s0.M, a0.ND);
+        d.bits = s0.bits + (size_t)k0 * d.plane;
+        d.alpha = s0.alpha + (size_t)k0 * s0.M;
+        d.al_bytes = (uint32_t)((size_t)KM * s0.M * 4);
+        d.wg0 = wg;
+        wg += (s0.M + 16 * RT - 1) / (16 * RT);
+      }
+    }
     for (int b0 = 0; b0 < a0.B; b0 += 16) {
       ProdArgs a = as;
       a.b0 = b0;

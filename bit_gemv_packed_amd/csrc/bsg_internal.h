@@ -128,6 +128,8 @@ hipError_t launch_prod_multi(const ProdArgs& a, hipStream_t s);
 // bf16 / fp16 x, no column scales.
 bool mfma_eligible(int B, int xdt, bool colscale);
 hipError_t launch_prod_mfma(const ProdArgs& a, hipStream_t s);
+// The matrix-core path can fuse projections (a.np > 1) for this B and x.
+bool mfma_multi_ok(int B, const void* x);
 hipError_t launch_prod_i8(const ProdArgs& a, const ProdPlan& p, hipStream_t s);
 
 }  // namespace bsg

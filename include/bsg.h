@@ -231,7 +231,9 @@ BSG_API bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const floa
  * what bs_gemv would write, within the same bound (the fused plan may sum in
  * another order).  The grid holds the row blocks of every projection in
  * turn, so small projections share one launch and its latency.  With B > 1
- * batch columns the projections are launched one after another.
+ * batch columns one fused launch is made per 16 columns on the matrix-core
+ * path (B % 4 == 0, x 8-byte aligned); otherwise the projections are
+ * launched one after another.
  */
 typedef struct bsg_proj {
   const uint32_t* bits;

@@ -4,8 +4,9 @@ projection's y against the CPU oracle, within the bs_gemv bound.
 Cases cover projections of different heights sharing x (query/key/value and
 gated-MLP shapes, scaled down), ragged heights, an empty projection between
 others, eight projections, column scales on every projection, K = 1..6,
-batch width 1 (one fused launch) and 2 and 4 (a launch per projection, the
-latter on the matrix cores), fp32/fp16/bf16 x, and accumulation.
+batch width 1 (one fused launch), 2 and 6 (a launch per projection) and 4,
+16 and 20 (fused on the matrix cores: a launch per 16 columns and 4 bases),
+fp32/fp16/bf16 x, and accumulation.
 """
 import numpy as np
 import pytest
@@ -29,6 +30,9 @@ MULTI_CASES = [
     (2, (128, 64), 256, 4, False, "bf16"),
     (6, (100, 50), 256, 1, True, "bf16"),
     (2, (4096, 1024, 1024), 4096, 1, False, "bf16"),
+    (2, (300, 64, 64), 1024, 16, False, "bf16"),
+    (6, (100, 40, 70), 512, 20, False, "f16"),
+    (3, (90, 33), 256, 6, False, "bf16"),
 ]
 
 
