@@ -509,9 +509,10 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8) {
   }
   p.RW = 64 / p.Q;
   const int KX = (colscale && !i8) ? K : 1;
-  // 8-word chunks (256 columns) for one batch column and K <= 2; 4-word
-  // chunks otherwise (smaller tables and register sets)
-  p.CW = (p.BB == 1 && p.KM <= 2) ? 8 : 4;
+  // 8-word chunks (256 columns) for one batch column and K <= 2, and for
+  // K <= 4 with 2 or 4 lanes per row and one table set (no column scales);
+  // 4-word chunks otherwise (smaller tables and register sets)
+  p.CW = (p.BB == 1 && (p.KM <= 2 || (!i8 && p.KM <= 4 && p.Q >= 2 && KX == 1))) ? 8 : 4;
   p.NWL = p.CW / p.Q;
   p.wave_lds = i8 ? (size_t)p.CW * p.BB * 12 * 4 : (size_t)KX * p.BB * (p.NWL * 8) * (p.Q * 64 + 16);
   const int T = (ND + p.CW - 1) / p.CW;  // chunks

@@ -166,15 +166,17 @@ inline hipError_t launch_one(Kern kern, const ProdPlan& p, const ProdArgs& a, hi
 }
 
 // Every kernel instance the planner may choose.  One batch column: 8-word
-// chunks for K <= 2, 4-word chunks otherwise; XM = 1 / 2 select the aligned
-// bf16 / fp16 single-column activation path of the float kernel.  Several
-// batch columns: 4-word chunks, generic activation path.
+// chunks for K <= 2, and for K <= 4 with Q >= 2 and no column scales, 4-word
+// chunks otherwise; XM = 1 / 2 select the aligned bf16 / fp16 single-column
+// activation path of the float kernel.  Several batch columns: 4-word
+// chunks, generic activation path.
 #define BSG_PROD_XM(X, Q, NWL, KM) X(Q, NWL, KM, 1, 0) X(Q, NWL, KM, 1, 1) X(Q, NWL, KM, 1, 2)
 #define BSG_PROD_F_ONE_COLUMN(X)                                                                             \
   BSG_PROD_XM(X, 4, 2, 1) BSG_PROD_XM(X, 4, 2, 2) BSG_PROD_XM(X, 2, 4, 1) BSG_PROD_XM(X, 2, 4, 2)            \
-  BSG_PROD_XM(X, 1, 8, 1) BSG_PROD_XM(X, 1, 8, 2) BSG_PROD_XM(X, 4, 1, 3) BSG_PROD_XM(X, 4, 1, 4)            \
-  BSG_PROD_XM(X, 4, 1, 8) BSG_PROD_XM(X, 2, 2, 3) BSG_PROD_XM(X, 2, 2, 4) BSG_PROD_XM(X, 2, 2, 8)            \
-  BSG_PROD_XM(X, 1, 4, 3) BSG_PROD_XM(X, 1, 4, 4) BSG_PROD_XM(X, 1, 4, 8)
+  BSG_PROD_XM(X, 1, 8, 1) BSG_PROD_XM(X, 1, 8, 2) BSG_PROD_XM(X, 4, 2, 3) BSG_PROD_XM(X, 4, 2, 4)            \
+  BSG_PROD_XM(X, 4, 1, 8) BSG_PROD_XM(X, 2, 4, 3) BSG_PROD_XM(X, 2, 4, 4) BSG_PROD_XM(X, 2, 2, 8)            \
+  BSG_PROD_XM(X, 1, 4, 3) BSG_PROD_XM(X, 1, 4, 4) BSG_PROD_XM(X, 1, 4, 8) BSG_PROD_XM(X, 4, 1, 3)            \
+  BSG_PROD_XM(X, 4, 1, 4) BSG_PROD_XM(X, 2, 2, 3) BSG_PROD_XM(X, 2, 2, 4)
 #define BSG_PROD_F_INSTANCES(X) BSG_PROD_F_ONE_COLUMN(X) BSG_PROD_MULTI_B(X, 2) BSG_PROD_I8_MULTI_B(X, 4)
 #define BSG_PROD_I8_INSTANCES(X)                                                                       \
   X(4, 2, 1, 1, 0) X(4, 2, 2, 1, 0) X(2, 4, 1, 1, 0) X(2, 4, 2, 1, 0) X(1, 8, 1, 1, 0) X(1, 8, 2, 1, 0) \

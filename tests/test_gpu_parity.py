@@ -59,6 +59,10 @@ GEMV_CASES = [
     (5, 77, 320, 3, False, "bf16", "normal"),
     (2, 17000, 256, 1, True, "bf16", "normal"),
     (1, 9000, 96, 2, False, "f16", "normal"),
+    (3, 257, 1056, 1, False, "bf16", "normal"),
+    (4, 130, 2080, 1, False, "f16", "normal"),
+    (4, 200, 544, 1, False, "f32", "student_t3"),
+    (3, 17000, 256, 1, False, "bf16", "normal"),
 ]
 
 
