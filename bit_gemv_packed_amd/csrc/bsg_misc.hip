@@ -1,75 +1,150 @@
 // Protected int8 rows, int8 activation quantisation and layout conversions
 // for gfx950.
+#include <algorithm>
+
 #include "bsg_internal.h"
 
 namespace bsg {
 
+// Sum over the workgroup of one value per thread (blockDim.x = 64 W), in a
+// fixed order: a butterfly inside each wavefront, then the W wavefront sums
+// in index order.  Every thread gets the result.  red: >= 16 floats of LDS.
+template <bool MAX>
+__device__ inline float block_reduce(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float u = __shfl_xor(v, o);
+    v = MAX ? fmaxf(v, u) : v + u;
+  }
+  const int wv = threadIdx.x >> 6, W = blockDim.x >> 6;
+  __syncthreads();  // red may still be read from a previous call
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  __syncthreads();
+  float t = red[0];
+  for (int w = 1; w < W; ++w) t = MAX ? fmaxf(t, red[w]) : t + red[w];
+  return t;
+}
+
+// 8 consecutive 16-bit x values (one aligned 16-byte load) -> fp32
+__device__ inline void load8_x16(const void* x, int xdt, size_t i, float (&v)[8]) {
+  const uint4 u = *(const uint4*)((const uint16_t*)x + i);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint16_t h = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+    v[j] = xdt == BSG_BF16 ? bf16_bits_to_float(h) : f16_bits_to_float(h);
+  }
+}
+
 // y[rows[i], b] += s_i * sum_n q[i][n] * x[n, b]   (BiSCo "Sensitivity
 // Protection": the protected rows are kept in 8 bits apart from the binary
-// payload).  One workgroup per protected row; int8 -> fp32 conversions are
-// exact; fp32 accumulation, fixed-order tree reduction.
-__global__ void __launch_bounds__(256) k_salient(const int32_t* __restrict__ rows, const int8_t* __restrict__ q,
-                                                 const uint16_t* __restrict__ s, int M, int N,
-                                                 const void* __restrict__ x, int xdt, int B, float* __restrict__ y) {
-  __shared__ float red[256];
+// payload).  One workgroup of 1024 threads per protected row; int8 -> fp32
+// conversions are exact; fp32 accumulation, fixed-order reduction.  VEC: one
+// batch column of 16-bit x, N % 16 == 0, q row and x 16-byte aligned: each
+// thread takes 16 columns with one 16-byte q load and two x loads.
+template <bool VEC>
+__global__ void __launch_bounds__(1024) k_salient(const int32_t* __restrict__ rows, const int8_t* __restrict__ q,
+                                                  const uint16_t* __restrict__ s, int M, int N,
+                                                  const void* __restrict__ x, int xdt, int B, float* __restrict__ y) {
+  __shared__ float red[16];
   const int i = blockIdx.x;
   const int m = rows[i];
   if (m < 0 || m >= M) return;
   const int8_t* qi = q + (size_t)i * N;
   const float si = f16_bits_to_float(s[i]);
-  const bool vec = ((N & 15) == 0) && ((((uintptr_t)qi) & 15) == 0);
+  if (VEC) {
+    float acc = 0.0f;
+    for (int n0 = threadIdx.x * 16; n0 < N; n0 += blockDim.x * 16) {
+      const int4 qv = *(const int4*)(qi + n0);
+      const int qw[4] = {qv.x, qv.y, qv.z, qv.w};
+      float xv[16];
+      load8_x16(x, xdt, n0, *(float(*)[8])xv);
+      load8_x16(x, xdt, n0 + 8, *(float(*)[8])(xv + 8));
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        acc = __builtin_fmaf((float)(int8_t)((uint32_t)qw[j >> 2] >> (8 * (j & 3))), xv[j], acc);
+    }
+    const float t = block_reduce<false>(acc, red);
+    if (threadIdx.x == 0) y[m] += si * t;
+    return;
+  }
   for (int b = 0; b < B; ++b) {
     float acc = 0.0f;
-    if (vec) {
-      for (int n0 = threadIdx.x * 16; n0 < N; n0 += 256 * 16) {
-        const int4 v = *(const int4*)(qi + n0);
-        const int vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int qv = (int)(int8_t)((uint32_t)vv[c] >> (8 * j));
-            acc += (float)qv * load_x(x, xdt, (size_t)(n0 + c * 4 + j) * B + b);
-          }
-        }
-      }
-    } else {
-      for (int n = threadIdx.x; n < N; n += 256) acc += (float)qi[n] * load_x(x, xdt, (size_t)n * B + b);
-    }
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-      if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) y[(size_t)m * B + b] += si * red[0];
-    __syncthreads();
+    for (int n = threadIdx.x; n < N; n += blockDim.x)
+      acc = __builtin_fmaf((float)qi[n], load_x(x, xdt, (size_t)n * B + b), acc);
+    const float t = block_reduce<false>(acc, red);
+    if (threadIdx.x == 0) y[(size_t)m * B + b] += si * t;
   }
 }
 
 // sx[b] = fp32(max_n |x| / 127); xq = clamp(rint_even(fp32(x / sx)), -127, 127).
-__global__ void __launch_bounds__(256) k_quantize(const void* __restrict__ x, int xdt, int N, int B,
-                                                  int8_t* __restrict__ xq, float* __restrict__ sx) {
-  __shared__ float red[256];
+// One workgroup of 1024 threads per batch column.  VEC: one batch column of
+// 16-bit x, N % 8 == 0, x 16-byte and xq 8-byte aligned: 8 values per thread
+// and pass, kept in registers between the two phases.
+template <bool VEC>
+__global__ void __launch_bounds__(1024) k_quantize(const void* __restrict__ x, int xdt, int N, int B,
+                                                   int8_t* __restrict__ xq, float* __restrict__ sx) {
+  __shared__ float red[16];
   const int b = blockIdx.x;
-  float mx = 0.0f;
-  for (int n = threadIdx.x; n < N; n += 256) mx = fmaxf(mx, fabsf(load_x(x, xdt, (size_t)n * B + b)));
-  red[threadIdx.x] = mx;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + off]);
-    __syncthreads();
-  }
-  const float s = __fdiv_rn(red[0], 127.0f);
-  if (threadIdx.x == 0) sx[b] = s;
-  for (int n = threadIdx.x; n < N; n += 256) {
-    int8_t v = 0;
-    if (s != 0.0f) {
-      float r = __builtin_rintf(__fdiv_rn(load_x(x, xdt, (size_t)n * B + b), s));
-      r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
-      v = (int8_t)r;
+  if (VEC) {
+    constexpr int P = 4;  // passes kept in registers (N <= 32768); larger N re-reads x
+    float v[P][8];
+    float mx = 0.0f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int n0 = (p * blockDim.x + threadIdx.x) * 8;
+      if (n0 < N) {
+        load8_x16(x, xdt, n0, v[p]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(v[p][j]));
+      }
     }
-    xq[(size_t)n * B + b] = v;
+    for (int n0 = (P * blockDim.x + threadIdx.x) * 8; n0 < N; n0 += blockDim.x * 8) {
+      float u[8];
+      load8_x16(x, xdt, n0, u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(u[j]));
+    }
+    const float sv = __fdiv_rn(block_reduce<true>(mx, red), 127.0f);
+    if (threadIdx.x == 0) sx[0] = sv;
+    auto quant8 = [&](const float (&u)[8], int n0) {
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        int c = 0;
+        if (sv != 0.0f) {
+          float r = __builtin_rintf(__fdiv_rn(u[j], sv));
+          r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+          c = (int)r;
+        }
+        w[j >> 2] |= ((uint32_t)c & 0xffu) << (8 * (j & 3));
+      }
+      *(uint2*)(xq + n0) = make_uint2(w[0], w[1]);
+    };
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int n0 = (p * blockDim.x + threadIdx.x) * 8;
+      if (n0 < N) quant8(v[p], n0);
+    }
+    for (int n0 = (P * blockDim.x + threadIdx.x) * 8; n0 < N; n0 += blockDim.x * 8) {
+      float u[8];
+      load8_x16(x, xdt, n0, u);
+      quant8(u, n0);
+    }
+    return;
+  }
+  float mx = 0.0f;
+  for (int n = threadIdx.x; n < N; n += blockDim.x) mx = fmaxf(mx, fabsf(load_x(x, xdt, (size_t)n * B + b)));
+  const float sv = __fdiv_rn(block_reduce<true>(mx, red), 127.0f);
+  if (threadIdx.x == 0) sx[b] = sv;
+  for (int n = threadIdx.x; n < N; n += blockDim.x) {
+    int8_t c = 0;
+    if (sv != 0.0f) {
+      float r = __builtin_rintf(__fdiv_rn(load_x(x, xdt, (size_t)n * B + b), sv));
+      r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+      c = (int8_t)r;
+    }
+    xq[(size_t)n * B + b] = c;
   }
 }
 
@@ -106,14 +181,26 @@ static int grid_for(size_t n, int threads) {
   return (int)(g ? g : 1);
 }
 
+static bool aligned(const void* p, size_t a) { return (((uintptr_t)p) % a) == 0; }
+
 hipError_t launch_salient_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s, int M, int N,
                                 const void* x, int xdt, int B, float* y, hipStream_t st) {
-  hipLaunchKernelGGL(k_salient, dim3(ns), dim3(256), 0, st, rows, q, s, M, N, x, xdt, B, y);
+  const bool vec = B == 1 && xdt != BSG_F32 && N % 16 == 0 && aligned(q, 16) && aligned(x, 16);
+  const int threads = std::min(1024, std::max(64, (N / (vec ? 16 : 1) + 63) / 64 * 64));
+  if (vec)
+    hipLaunchKernelGGL(k_salient<true>, dim3(ns), dim3(threads), 0, st, rows, q, s, M, N, x, xdt, B, y);
+  else
+    hipLaunchKernelGGL(k_salient<false>, dim3(ns), dim3(threads), 0, st, rows, q, s, M, N, x, xdt, B, y);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize(const void* x, int xdt, int N, int B, int8_t* xq, float* sx, hipStream_t st) {
-  hipLaunchKernelGGL(k_quantize, dim3(B), dim3(256), 0, st, x, xdt, N, B, xq, sx);
+  const bool vec = B == 1 && xdt != BSG_F32 && N % 8 == 0 && aligned(x, 16) && aligned(xq, 8);
+  const int threads = std::min(1024, std::max(64, (N / (vec ? 8 : 1) + 63) / 64 * 64));
+  if (vec)
+    hipLaunchKernelGGL(k_quantize<true>, dim3(B), dim3(threads), 0, st, x, xdt, N, B, xq, sx);
+  else
+    hipLaunchKernelGGL(k_quantize<false>, dim3(B), dim3(threads), 0, st, x, xdt, N, B, xq, sx);
   return hipGetLastError();
 }
 

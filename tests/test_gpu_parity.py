@@ -181,8 +181,11 @@ def test_bs_gemv_i8_exact(case):
 
 
 def test_quantize_i8_bit_exact():
+    # one 16-bit column with N % 8 == 0 takes the vector path (registers up to
+    # N = 32768, then a second read of x); the others the generic one
     for (N, B, dt, dist) in [(4096, 1, "bf16", "normal"), (5120, 16, "bf16", "student_t3"), (96, 3, "f32", "normal"),
-                             (256, 2, "f16", "normal")]:
+                             (256, 2, "f16", "normal"), (8, 1, "f16", "normal"), (1024, 1, "f16", "student_t3"),
+                             (40000, 1, "bf16", "normal"), (4100, 1, "bf16", "normal"), (4096, 1, "f32", "normal")]:
         say("quantize", N, B, dt, dist)
         x = synth.random_x(N + B, N, B, dt, dist)
         xq, sx = bsg.bsq_quantize_i8(x_dev(x, dt))
@@ -219,7 +222,8 @@ def test_binlr_apply_matches_oracle(case):
 
 
 # ------------------------------------------------------------------ protected rows
-SAL_CASES = [(256, 256, 3, 1), (13824, 5120, 138, 1), (100, 100, 5, 2), (5120, 13824, 51, 16), (64, 32, 64, 1)]
+SAL_CASES = [(256, 256, 3, 1), (13824, 5120, 138, 1), (100, 100, 5, 2), (5120, 13824, 51, 16), (64, 32, 64, 1),
+             (64, 48, 3, 1), (300, 100, 7, 1), (5120, 13824, 51, 1)]
 
 
 @pytest.mark.parametrize("case", SAL_CASES, ids=lambda c: "M%d_N%d_ns%d_B%d" % c)
