@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
                "s"(a.N), "s"(a.ND), "s"(a.B), "s"(a.b0), "s"(a.xdt), "s"(a.NCH), "s"(a.wave_lds), "s"(a.x_bytes),
                "s"(a.cs_bytes), "s"(a.al_bytes));
   // fused launch: this workgroup's projection and its block within it
-  int blk = blockIdx.x;
+  uint32_t blk = blockIdx.x;
   if (MP) {
     // constant indices only (a computed index would copy the arguments to
     // scratch memory)
@@ -282,7 +282,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wavefront index (uniform)
   const int q = lane / RW;
   const int r = lane % RW;
-  const int m = blk * RW + r;
+  const int m = (int)(blk * RW + r);
   const bool valid = m < a.M;
   // rows beyond M read padding; their sums are dropped
   const SignRows<KM> srows = sign_rows<KM, RW>(a.bits, a.plane, a.K, a.ND, blk, m);
@@ -401,7 +401,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
     const rsrc_t rs = make_rsrc(a.sal_rows, (size_t)a.sal_n * 4);
     const rsrc_t qs = make_rsrc(a.sal_q, (size_t)a.sal_n * a.N);
     const rsrc_t ss = make_rsrc(a.sal_s, (size_t)a.sal_n * 2);
-    const int m0 = blk * RW;
+    const int m0 = (int)(blk * RW);
     const int i0 = lower_bound_rows(rs, a.sal_n, m0, lane);
     const int i1 = lower_bound_rows(rs, a.sal_n, m0 + RW, lane);
     for (int i = i0 + wv; i < i1; i += a.W) {
@@ -464,7 +464,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB), (KM <= 2 && BB ==
   __syncthreads();
   for (int t = threadIdx.x; t < RW * BB; t += blockDim.x) {  // blockDim may be below RW * BB
     const int rr = t / BB, b = t % BB;
-    const int mm = blk * RW + rr;
+    const int mm = (int)(blk * RW + rr);
     if (mm < a.M && a.b0 + b < a.B) {
       const float s = sum_waves(red + rr * BB + b, RW * BB, a.W);
       const size_t yi = (size_t)mm * a.B + a.b0 + b;

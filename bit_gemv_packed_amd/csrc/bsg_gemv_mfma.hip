@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(64 * mfma_max_waves(RT, KM, VW)) k_prod_mfma(P
                "s"(a.ND), "s"(a.B), "s"(a.b0), "s"(a.accumulate), "s"(a.NCH), "s"(a.x_bytes), "s"(a.al_bytes));
   // fused launch: this workgroup's projection (constant indices only: a
   // computed index would copy the arguments to scratch memory)
-  int blk = blockIdx.x;
+  uint32_t blk = blockIdx.x;
   if (MP) {
     ProjDesc d = a.proj[0];
 #pragma unroll
@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(64 * mfma_max_waves(RT, KM, VW)) k_prod_mfma(P
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int m0 = blk * 16 * RT;
+  const int m0 = (int)(blk * 16 * RT);
   const uint32_t xt = (uint32_t)(uintptr_t)lds + (uint32_t)wv * kXtBytes;
   uint32_t msk;
   asm volatile("s_mov_b32 %0, 0x80008000" : "=s"(msk));

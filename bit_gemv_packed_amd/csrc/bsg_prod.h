@@ -79,8 +79,8 @@ __device__ inline SignRows<KM> sign_rows_in(const uint32_t* bits, size_t plane, 
 }
 // workgroup blk (uniform) owns rows [blk RW, blk RW + RW)
 template <int KM, int RW>
-__device__ inline SignRows<KM> sign_rows(const uint32_t* bits, size_t plane, int K, int ND, int blk, int m) {
-  return sign_rows_in<KM>(bits, plane, K, ND, (blk * RW) >> 6, m);
+__device__ inline SignRows<KM> sign_rows(const uint32_t* bits, size_t plane, int K, int ND, uint32_t blk, int m) {
+  return sign_rows_in<KM>(bits, plane, K, ND, (int)(blk * RW) >> 6, m);
 }
 
 // Sign words of one chunk: NWL consecutive logical words [w0, w0 + NWL) of
