@@ -64,6 +64,7 @@ def lib():
             "or_layout_offset": (_SZ, [_I, _I, _I, _I, _I, _I]),
             "or_logical_to_layout": (None, [_P, _I, _I, _I, _P]),
             "or_layout_to_logical": (None, [_P, _I, _I, _I, _P]),
+            "or_binlr_fit": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -231,6 +232,28 @@ def salient_select(W, xbar, ns: int, alpha=None):
 
 
 # ---------------------------------------------------------------- layout
+def binlr_fit(W, r: int, vinit, rounds: int = 5):
+    """Offline binary low-rank fit (BiLoCo "Finding the sign vectors", "Joint
+    refit"); see or_binlr_fit.  W: fp32 [M][N] (any N > 0); vinit: logical
+    sign words [r][ceil(N/32)] of the start vectors.  Returns (ubits [M][ceil(r/32)], vbits
+    [r][N/32], alpha_greedy [r], alpha [r] refitted, (sse_greedy, sse_refit),
+    solved)."""
+    W = _c(np.asarray(W, np.float32), np.float32)
+    M, N = W.shape
+    rd, nd = (r + 31) // 32, (N + 31) // 32
+    vinit = _c(np.asarray(vinit, np.uint32).reshape(r, nd), np.uint32)
+    ub = np.zeros((M, rd), np.uint32)
+    vb = np.zeros((r, nd), np.uint32)
+    ag = np.zeros(r, np.float64)
+    al = np.zeros(r, np.float64)
+    sse = np.zeros(2, np.float64)
+    rc = lib().or_binlr_fit(_ptr(W), M, N, r, rounds, _ptr(vinit), _ptr(ub), _ptr(vb), _ptr(ag), _ptr(al),
+                            _ptr(sse))
+    if rc < 0:
+        raise ValueError("binlr_fit: bad sizes")
+    return ub, vb, ag, al, (float(sse[0]), float(sse[1])), bool(rc)
+
+
 def layout_words(K, M, N) -> int:
     return K * int(lib().or_layout_plane_words(M, N))
 

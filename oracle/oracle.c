@@ -11,8 +11,9 @@
  * Sources (the web pages this path is built from):
  *  [BiLoCo]  "BiLoCo: Binary Low-Rank Corrections for Post-Training
  *            Quantization", sections "The core idea" (alpha*u*(v.x) computed
- *            with additions only; worked example) and "Finding the sign
- *            vectors" (error-minimising coefficient).
+ *            with additions only; worked example), "Finding the sign
+ *            vectors" (greedy alternating signs, error-minimising
+ *            coefficient) and "Joint refit".
  *  [FluxBin] "FluxBin: Flexible LUT-based Ultra-low-bit LLM Inference by
  *            Algorithm-Kernel Synergy", Sec. 2 (greedy residual binary bases,
  *            R(k) = R(k-1) - alpha_k B(k)), Sec. 3.1 (decoupled row/column
@@ -438,6 +439,144 @@ OR_API void or_layout_to_logical(const uint32_t* phys, int K, int M, int N, uint
     for (int m = 0; m < M; ++m)
       for (size_t w = 0; w < nd; ++w)
         logical[((size_t)k * M + m) * nd + w] = phys[or_layout_offset(K, M, N, k, m, (int)w)];
+}
+
+/* ------------------------------------------------------------------ */
+/* Offline fit of the binary low-rank correction.                       */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [BiLoCo, "Finding the sign vectors" and "Joint refit"]: rank-one sign
+ * components found one at a time on the residual, then every coefficient
+ * refitted at once.
+ *   R = W                                             (double)
+ *   for j = 0 .. r-1:
+ *     v = the j-th given start vector (vinit row j; bit 1 -> +1, 0 -> -1)
+ *     repeat `rounds` times:  u = sign(R v);  v = sign(R^T u)
+ *                             (sign(0) = +1; sums in ascending index order)
+ *     alpha_j = u^T R v / (M N)                       (the error-minimising
+ *               coefficient of a +-1 rank-one term; with the last R^T u = b
+ *               and v = sign(b) it equals sum_n |b_n| / (M N))
+ *     R = R - alpha_j u v^T
+ *   joint refit: alpha minimises || W - sum_j alpha_j u_j v_j^T ||_F, i.e.
+ *     G alpha = c with G_ij = (u_i . u_j)(v_i . v_j), c_j = u_j^T W v_j,
+ *     solved by Gaussian elimination with partial pivoting.  If a pivot is
+ *     below 1e-12 * max_i G_ii the system counts as singular and the greedy
+ *     coefficients are kept (reading: the pages do not treat that case).
+ * The random start vectors are an input (drawn by the caller).
+ * Out: ubits logical [M][ceil(r/32)] (bit j of row m = u_j[m]), vbits logical
+ * [r][ceil(N/32)] (any N > 0), alpha_greedy[r], alpha[r] (refit), sse[0] = ||R||^2 after the
+ * greedy pass, sse[1] = the squared error with the refitted coefficients.
+ * Returns 1 if the refit was solved, 0 if it kept the greedy coefficients,
+ * -1 on bad sizes.
+ */
+OR_API int or_binlr_fit(const float* W, int M, int N, int r, int rounds, const uint32_t* vinit,
+                        uint32_t* ubits, uint32_t* vbits, double* alpha_greedy, double* alpha, double* sse) {
+  if (M <= 0 || N <= 0 || r <= 0 || rounds < 1) return -1;
+  const int nd = (N + 31) / 32, rd = (r + 31) / 32;
+  double* R = (double*)malloc(sizeof(double) * (size_t)M * N);
+  double* b = (double*)malloc(sizeof(double) * N);
+  signed char* U = (signed char*)malloc((size_t)M * r);  /* U[m * r + j] = u_j[m] */
+  signed char* V = (signed char*)malloc((size_t)r * N);  /* V[j * N + n] = v_j[n] */
+  for (size_t i = 0; i < (size_t)M * N; ++i) R[i] = (double)W[i];
+  for (int j = 0; j < r; ++j) {
+    signed char* v = V + (size_t)j * N;
+    for (int n = 0; n < N; ++n) v[n] = ((vinit[(size_t)j * nd + (n >> 5)] >> (n & 31)) & 1u) ? 1 : -1;
+    for (int t = 0; t < rounds; ++t) {
+      for (int m = 0; m < M; ++m) {
+        double a = 0.0;
+        for (int n = 0; n < N; ++n) a += R[(size_t)m * N + n] * (double)v[n];
+        U[(size_t)m * r + j] = a >= 0.0 ? 1 : -1;
+      }
+      for (int n = 0; n < N; ++n) {
+        double c = 0.0;
+        for (int m = 0; m < M; ++m) c += R[(size_t)m * N + n] * (double)U[(size_t)m * r + j];
+        b[n] = c;
+        v[n] = c >= 0.0 ? 1 : -1;
+      }
+    }
+    double num = 0.0;  /* u^T R v = sum_n b_n v_n */
+    for (int n = 0; n < N; ++n) num += b[n] * (double)v[n];
+    const double aj = num / ((double)M * (double)N);
+    alpha_greedy[j] = aj;
+    for (int m = 0; m < M; ++m)
+      for (int n = 0; n < N; ++n) R[(size_t)m * N + n] -= aj * (double)U[(size_t)m * r + j] * (double)v[n];
+  }
+  double s0 = 0.0;
+  for (size_t i = 0; i < (size_t)M * N; ++i) s0 += R[i] * R[i];
+  sse[0] = s0;
+
+  /* joint refit: normal equations, augmented matrix [G | c] */
+  double* A = (double*)malloc(sizeof(double) * (size_t)r * (r + 1));
+  double gmax = 0.0;
+  for (int i = 0; i < r; ++i) {
+    for (int j = 0; j < r; ++j) {
+      long long du = 0, dv = 0;
+      for (int m = 0; m < M; ++m) du += (long long)U[(size_t)m * r + i] * U[(size_t)m * r + j];
+      for (int n = 0; n < N; ++n) dv += (long long)V[(size_t)i * N + n] * V[(size_t)j * N + n];
+      A[(size_t)i * (r + 1) + j] = (double)du * (double)dv;
+    }
+    double c = 0.0;
+    for (int m = 0; m < M; ++m) {
+      double w = 0.0;
+      for (int n = 0; n < N; ++n) w += (double)W[(size_t)m * N + n] * (double)V[(size_t)i * N + n];
+      c += (double)U[(size_t)m * r + i] * w;
+    }
+    A[(size_t)i * (r + 1) + r] = c;
+    if (A[(size_t)i * (r + 1) + i] > gmax) gmax = A[(size_t)i * (r + 1) + i];
+  }
+  int solved = 1;
+  for (int k = 0; k < r && solved; ++k) {
+    int p = k;
+    for (int i = k + 1; i < r; ++i)
+      if (fabs(A[(size_t)i * (r + 1) + k]) > fabs(A[(size_t)p * (r + 1) + k])) p = i;
+    if (fabs(A[(size_t)p * (r + 1) + k]) < 1e-12 * gmax) {
+      solved = 0;
+      break;
+    }
+    if (p != k)
+      for (int j = 0; j <= r; ++j) {
+        double t = A[(size_t)k * (r + 1) + j];
+        A[(size_t)k * (r + 1) + j] = A[(size_t)p * (r + 1) + j];
+        A[(size_t)p * (r + 1) + j] = t;
+      }
+    for (int i = k + 1; i < r; ++i) {
+      const double f = A[(size_t)i * (r + 1) + k] / A[(size_t)k * (r + 1) + k];
+      for (int j = k; j <= r; ++j) A[(size_t)i * (r + 1) + j] -= f * A[(size_t)k * (r + 1) + j];
+    }
+  }
+  if (solved) {
+    for (int i = r - 1; i >= 0; --i) {
+      double t = A[(size_t)i * (r + 1) + r];
+      for (int j = i + 1; j < r; ++j) t -= A[(size_t)i * (r + 1) + j] * alpha[j];
+      alpha[i] = t / A[(size_t)i * (r + 1) + i];
+    }
+  } else {
+    for (int j = 0; j < r; ++j) alpha[j] = alpha_greedy[j];
+  }
+  double s1 = 0.0;
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n) {
+      double e = (double)W[(size_t)m * N + n];
+      for (int j = 0; j < r; ++j) e -= alpha[j] * (double)U[(size_t)m * r + j] * (double)V[(size_t)j * N + n];
+      s1 += e * e;
+    }
+  sse[1] = s1;
+
+  memset(ubits, 0, sizeof(uint32_t) * (size_t)M * rd);
+  memset(vbits, 0, sizeof(uint32_t) * (size_t)r * nd);
+  for (int m = 0; m < M; ++m)
+    for (int j = 0; j < r; ++j)
+      if (U[(size_t)m * r + j] > 0) ubits[(size_t)m * rd + (j >> 5)] |= 1u << (j & 31);
+  for (int j = 0; j < r; ++j)
+    for (int n = 0; n < N; ++n)
+      if (V[(size_t)j * N + n] > 0) vbits[(size_t)j * nd + (n >> 5)] |= 1u << (n & 31);
+  free(A);
+  free(V);
+  free(U);
+  free(b);
+  free(R);
+  return solved;
 }
 
 /* Array forms of the binary16 conversions. */

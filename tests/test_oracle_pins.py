@@ -440,3 +440,132 @@ def test_tolerance_reduces_to_row_bound():
     t = oracle.tolerance(x, alpha=alpha)
     ref = 2e-3 * np.abs(alpha.astype(np.float64)).sum(0) * np.abs(x).sum()
     np.testing.assert_allclose(t[:, 0], ref, rtol=1e-12)
+
+
+# ----------------------------------------------------------- low-rank fit (offline)
+def _signs_of_bits(words, n):
+    w = np.asarray(words, np.uint32).reshape(-1)
+    return np.array([1.0 if (w[i >> 5] >> (i & 31)) & 1 else -1.0 for i in range(n)])
+
+
+def _fit_factors(ub, vb, M, N, r):
+    U = np.stack([_signs_of_bits(ub[m], r) for m in range(M)])          # [M][r]
+    V = np.stack([_signs_of_bits(vb[j], N) for j in range(r)])          # [r][N]
+    return U, V
+
+
+def test_lr_fit_toy_example():
+    """Every value the page prints for its 3 x 2 example."""
+    g = _golden("biloco_toy_fit.txt")
+    W = np.array(g["W_rows"], np.float32).reshape(3, 2)
+    vinit = np.array([[_signs_to_word(g["v_start"])]] * 2, np.uint32)
+    ub, vb, ag, al, (sse_g, sse_r), solved = oracle.binlr_fit(W, 2, vinit)
+    U, V = _fit_factors(ub, vb, 3, 2, 2)
+    num, den = g["component1_alpha_num_den"]
+    np.testing.assert_array_equal(U[:, 0], g["component1_u"])
+    np.testing.assert_array_equal(W.astype(np.float64) @ np.array(g["v_start"]), g["component1_Rv"])
+    np.testing.assert_array_equal(W.astype(np.float64).T @ U[:, 0], g["component1_RTu"])
+    assert ag[0] == num / den == 2.0
+    R1 = W.astype(np.float64) - ag[0] * np.outer(U[:, 0], V[0])
+    np.testing.assert_array_equal(R1.ravel(), g["residual_rows"])
+    np.testing.assert_array_equal(U[:, 1], g["component2_u"])
+    np.testing.assert_array_equal(V[1], g["component2_v"])
+    num, den = g["component2_alpha_num_den"]
+    assert abs(ag[1] - num / den) < 1e-15
+    assert round(ag[1], 2) == g["component2_alpha_approx"][0]
+    assert abs(sse_g - 4.0 / 3.0) < 1e-12 and round(sse_g, 2) == g["greedy_sse_approx"][0]
+    assert solved
+    np.testing.assert_allclose(al, g["refit_alpha"], rtol=0, atol=1e-12)
+    assert abs(sse_r - g["refit_sse"][0]) < 1e-20
+
+
+def test_lr_fit_recovers_a_signed_rank_one_matrix():
+    """W = a u v^T with sign vectors: one component recovers it exactly (up
+    to flipping both signs), alpha = a, no error left."""
+    rng = np.random.default_rng(11)
+    M, N, a = 40, 64, 0.75
+    u = np.where(rng.integers(0, 2, M) == 1, 1.0, -1.0)
+    v = np.where(rng.integers(0, 2, N) == 1, 1.0, -1.0)
+    W = (a * np.outer(u, v)).astype(np.float32)
+    vinit = synth.random_bits(5, 1, 1, N)[0]
+    ub, vb, ag, al, (sse_g, sse_r), solved = oracle.binlr_fit(W, 1, vinit)
+    U, V = _fit_factors(ub, vb, M, N, 1)
+    s = U[0, 0] * u[0]
+    np.testing.assert_array_equal(U[:, 0], s * u)
+    np.testing.assert_array_equal(V[0], s * v)
+    assert abs(ag[0] - a) < 1e-12 and abs(al[0] - a) < 1e-12
+    assert sse_g < 1e-20 and sse_r < 1e-20
+
+
+def test_lr_fit_one_round_is_the_alternation_rule():
+    """With one round: u = sign(W v_start), v = sign(W^T u), sign(0) = +1
+    (a zero row of W gives a zero sum), alpha = u^T W v / (M N)."""
+    rng = np.random.default_rng(12)
+    M, N = 24, 40
+    W = rng.standard_normal((M, N)).astype(np.float32)
+    W[5] = 0.0
+    vinit = synth.random_bits(6, 1, 1, N)[0]
+    ub, vb, ag, al, _, _ = oracle.binlr_fit(W, 1, vinit, rounds=1)
+    U, V = _fit_factors(ub, vb, M, N, 1)
+    v0 = _signs_of_bits(vinit, N)
+    Wd = W.astype(np.float64)
+    u = np.where(Wd @ v0 >= 0, 1.0, -1.0)
+    assert u[5] == 1.0
+    v = np.where(Wd.T @ u >= 0, 1.0, -1.0)
+    np.testing.assert_array_equal(U[:, 0], u)
+    np.testing.assert_array_equal(V[0], v)
+    assert abs(ag[0] - u @ Wd @ v / (M * N)) < 1e-12 * abs(ag[0])
+    assert ag[0] == al[0] or abs(ag[0] - al[0]) < 1e-12 * abs(ag[0])  # one component: refit = greedy
+
+
+def test_lr_fit_greedy_coefficients_are_least_squares_and_sse_falls():
+    """Each greedy alpha_j minimises ||R_j - alpha u_j v_j^T|| over alpha, so
+    the residual energy falls by (u^T R_j v)^2 / (M N) per component."""
+    rng = np.random.default_rng(13)
+    M, N, r = 30, 48, 5
+    W = rng.standard_normal((M, N)).astype(np.float32)
+    vinit = synth.random_bits(7, 1, r, N)[0]
+    ub, vb, ag, al, (sse_g, _), _ = oracle.binlr_fit(W, r, vinit)
+    U, V = _fit_factors(ub, vb, M, N, r)
+    R = W.astype(np.float64)
+    energy = [float((R ** 2).sum())]
+    for j in range(r):
+        A = np.outer(U[:, j], V[j])
+        best = (A * R).sum() / (A * A).sum()            # least squares over alpha, written out
+        assert abs(ag[j] - best) < 1e-12 * max(1.0, abs(best))
+        R = R - ag[j] * A
+        energy.append(float((R ** 2).sum()))
+    assert all(energy[i + 1] <= energy[i] + 1e-9 for i in range(r))
+    assert abs(sse_g - energy[-1]) < 1e-9 * energy[0]
+
+
+def test_lr_fit_refit_is_the_least_squares_solution():
+    """The refitted coefficients solve min ||W - sum alpha_j u_j v_j^T||_F,
+    checked against a generic least-squares solve over the vectorised rank-one
+    terms; the refit never does worse than the greedy coefficients."""
+    rng = np.random.default_rng(14)
+    M, N, r = 20, 32, 6
+    W = rng.standard_normal((M, N)).astype(np.float32)
+    vinit = synth.random_bits(8, 1, r, N)[0]
+    ub, vb, ag, al, (sse_g, sse_r), solved = oracle.binlr_fit(W, r, vinit)
+    assert solved
+    U, V = _fit_factors(ub, vb, M, N, r)
+    A = np.stack([np.outer(U[:, j], V[j]).ravel() for j in range(r)], 1)
+    ls, res, _, _ = np.linalg.lstsq(A, W.astype(np.float64).ravel(), rcond=None)
+    np.testing.assert_allclose(al, ls, rtol=1e-9, atol=1e-12)
+    assert abs(sse_r - float(res[0])) < 1e-9 * float(res[0])
+    assert sse_r <= sse_g + 1e-12
+
+
+def test_lr_fit_singular_refit_keeps_the_greedy_coefficients():
+    """A constant matrix: the first component takes all of it, the second
+    sees a zero residual (sign(0) = +1 gives the same all-plus vectors), so the
+    normal equations are singular and the greedy coefficients stay."""
+    M, N = 8, 32
+    W = np.full((M, N), 0.5, np.float32)
+    vinit = np.full((2, 1), 0xFFFFFFFF, np.uint32)
+    ub, vb, ag, al, (sse_g, sse_r), solved = oracle.binlr_fit(W, 2, vinit)
+    assert not solved
+    np.testing.assert_array_equal(ag, [0.5, 0.0])
+    np.testing.assert_array_equal(al, ag)
+    assert sse_g == 0.0 and sse_r == 0.0
