@@ -329,6 +329,26 @@ def run_rows(steps, warmup):
         del bits, alpha, xq, sx, y, xf
         torch.cuda.empty_cache()
 
+    # f4: the offline binary low-rank fit (greedy alternating signs, joint refit), eager, one call each
+    for name, M, N, r in [("5120x5120 r=512", 5120, 5120, 512), ("4096x4096 r=128", 4096, 4096, 128)]:
+        W = torch.randn((M, N), device=dev) * 0.02
+        vinit = torch.from_numpy(synth.random_bits(1, 1, r, N)[0].view("int32")).to(dev)
+        ws = bsg.new_workspace(int(bsg.lib().binlr_fit_workspace_bytes(M, N, r)) + 256, dev)
+        bsg.binlr_fit(W[:64], min(r, 32), vinit[:min(r, 32)], workspace=ws)   # first-call costs
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = bsg.binlr_fit(W, r, vinit, workspace=ws)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6
+        # per component: 5 rounds x 2 passes over the fp64 residual + the rank-one update (read + write),
+        # then one fp32 pass over W per component for the refit
+        passes = r * (5 * 2 * 8 * M * N + 16 * M * N + 4 * M * N)
+        emit("f4", "binlr_fit (offline, eager, one call)", name, us, passes, r=r,
+             sse_greedy_over_w2=round(res[6][0] / float((W.double() ** 2).sum()), 4),
+             sse_refit_over_w2=round(res[6][1] / float((W.double() ** 2).sum()), 4))
+        del W, vinit, ws, res
+        torch.cuda.empty_cache()
+
     # a0: packing (offline), eager
     W = torch.randn((4096, 4096), device=dev) * 0.02
     bsg.bsq_pack(W, 2, colscale=True)

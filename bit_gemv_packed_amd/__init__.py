@@ -56,6 +56,8 @@ _SIGS = {
     "bs_gemv": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P]),
     "bs_gemv_i8": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _I, _P]),
     "bs_gemv_multi": (ctypes.c_int32, [_P, _I, _I, _I, _P, _I, _I, _I, _P]),
+    "binlr_fit_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "binlr_fit": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "binlr_apply": (ctypes.c_int32, [_P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P, _SZ, _P]),
     "salient_int8_apply": (ctypes.c_int32, [_P, _I, _P, _P, _I, _I, _P, _I, _I, _P, _P]),
     "bsg_linear_workspace_bytes": (_SZ, [_I, _I]),
@@ -295,6 +297,35 @@ def bs_gemv_multi(projs, K: int, N: int, x, accumulate: bool = False):
     _check("bs_gemv_multi", lib().bs_gemv_multi(ctypes.cast(arr, ctypes.c_void_p), len(projs), K, N, _ptr(x),
                                                 _dtype_code(x), B, 1 if accumulate else 0, _stream(dev)))
     return ys
+
+
+def binlr_fit(W, r: int, v_init, rounds: int = 5, workspace=None):
+    """Offline binary low-rank fit of W (fp32 [M][N] on the GPU).  v_init: int32/uint32 device tensor of the
+    start vectors' logical sign words [r][N/32].  Returns (U_bits, V_bits, alpha_r_f16, rp, alpha, alpha_greedy,
+    (sse_greedy, sse_refit), solved): device-layout signs and fp16 coefficients for rp = r rounded up to 32
+    components (binlr_apply's inputs), and host numpy fp64 coefficients."""
+    import numpy as np
+    torch = _torch()
+    M, N = W.shape
+    dev = W.device
+    rp = (r + 31) // 32 * 32
+    U = torch.zeros(layout_words(1, M, rp), dtype=torch.int32, device=dev)
+    V = torch.zeros(layout_words(1, rp, N), dtype=torch.int32, device=dev)
+    a16 = torch.zeros(rp, dtype=torch.int16, device=dev)
+    al = np.zeros(r, np.float64)
+    ag = np.zeros(r, np.float64)
+    sse = np.zeros(2, np.float64)
+    solved = ctypes.c_int(0)
+    nb = int(lib().binlr_fit_workspace_bytes(M, N, r))
+    ws = workspace if workspace is not None else new_workspace(nb + 256, dev)
+    wp = ws.data_ptr()
+    wp_al = (wp + 255) // 256 * 256
+    wn = ws.numel() * ws.element_size() - (wp_al - wp)
+    _check("binlr_fit", lib().binlr_fit(_ptr(W), M, N, r, rounds, _ptr(v_init), _ptr(U), _ptr(V), _ptr(a16),
+                                        al.ctypes.data_as(ctypes.c_void_p), ag.ctypes.data_as(ctypes.c_void_p),
+                                        sse.ctypes.data_as(ctypes.c_void_p), ctypes.addressof(solved), wp_al, wn,
+                                        _stream(dev)))
+    return U, V, a16, rp, al, ag, (float(sse[0]), float(sse[1])), bool(solved.value)
 
 
 def bs_gemv_i8(bits, K: int, M: int, N: int, alpha, xq, sx, want_acc: bool = True, want_y: bool = True,

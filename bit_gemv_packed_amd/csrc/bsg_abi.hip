@@ -17,6 +17,11 @@ hipError_t launch_salient_apply(const int32_t* rows, int ns, const int8_t* q, co
                                 const void* x, int xdt, int B, float* y, hipStream_t st);
 hipError_t launch_quantize(const void* x, int xdt, int N, int B, int8_t* xq, float* sx, hipStream_t st);
 hipError_t launch_layout(const uint32_t* src, int K, int M, int N, uint32_t* dst, bool to_layout, hipStream_t st);
+size_t fit_workspace_bytes(int M, int N, int r);
+hipError_t launch_binlr_fit(const float* W, int M, int N, int r, int rounds, const uint32_t* v_init,
+                            uint32_t* U_bits, uint32_t* V_bits, uint16_t* alpha_f16, double* alpha_out,
+                            double* alpha_greedy_out, double* sse_out, int* solved_out, void* workspace,
+                            hipStream_t st);
 }  // namespace bsg
 
 using namespace bsg;
@@ -259,6 +264,24 @@ bsg_status bs_gemv_multi(const bsg_proj* projs, int P, int K, int N, const void*
   }
   a.np = np;
   return hip_status(launch_prod_multi(a, st));
+}
+
+size_t binlr_fit_workspace_bytes(int M, int N, int r) {
+  if (M < 1 || bad_n(N) || r < 1 || r > kMaxFitRank) return 0;
+  return fit_workspace_bytes(M, N, r);
+}
+
+bsg_status binlr_fit(const float* W, int M, int N, int r, int rounds, const uint32_t* v_init, uint32_t* U_bits,
+                     uint32_t* V_bits, uint16_t* alpha_r_f16, double* alpha, double* alpha_greedy, double* sse,
+                     int* solved, void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 1 || bad_n(N) || r < 1 || r > kMaxFitRank || rounds < 1 || rounds > 64) return BSG_ERR_SHAPE;
+  if (!W || !v_init || !U_bits || !V_bits || !alpha_r_f16) return BSG_ERR_NULL;
+  if (misaligned(W, 4) || misaligned(v_init, 4) || misaligned(U_bits, 16) || misaligned(V_bits, 16) ||
+      misaligned(alpha_r_f16, 2) || misaligned(workspace, 256))
+    return BSG_ERR_ALIGN;
+  if (!workspace || workspace_bytes < fit_workspace_bytes(M, N, r)) return BSG_ERR_WORKSPACE;
+  return hip_status(launch_binlr_fit(W, M, N, r, rounds, v_init, U_bits, V_bits, alpha_r_f16, alpha, alpha_greedy,
+                                     sse, solved, workspace, (hipStream_t)stream));
 }
 
 bsg_status bs_gemv_i8(const uint32_t* bits, int K, int M, int N, const float* alpha, const int8_t* xq,

@@ -14,6 +14,7 @@ constexpr int kRowBlock = 64;   // rows per layout tile = lanes per wavefront
 constexpr int kGroupWords = 4;  // words per layout tile (one 16-byte load per lane)
 constexpr int kMaxK = 8;
 constexpr int kMaxB = 64;
+constexpr int kMaxFitRank = 2048;  // binlr_fit: the r x r refit is solved on the host
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
 // Words of one base in the device layout: M*ND rounded up to 64 words.

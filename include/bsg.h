@@ -287,6 +287,42 @@ BSG_API bsg_status salient_int8_apply(const int32_t* rows, int ns, const int8_t*
                               void* stream);
 
 /*
+ * binlr_fit -- offline fit of the binary low-rank correction (BiLoCo,
+ * "Finding the sign vectors" and "Joint refit"):
+ *   R = W;  for j < r:  v = v_init[j];  `rounds` times { u = sign(R v);
+ *           v = sign(R^T u) };  alpha_j = u^T R v / (M N);  R -= alpha_j u v^T
+ *   then all coefficients refitted at once: alpha = argmin over alpha of
+ *   || W - sum_j alpha_j u_j v_j^T ||_F, from the normal equations
+ *   G alpha = c, G_ij = (u_i . u_j)(v_i . v_j), c_j = u_j^T W v_j (Gaussian
+ *   elimination with partial pivoting; if a pivot falls below 1e-12 max G_ii
+ *   the greedy coefficients are kept).  sign(0) = +1; the residual and all
+ *   sums are fp64.
+ *   W         (device) fp32 [M][N], row-major
+ *   v_init    (device) start vectors, logical sign words [r][N/32]
+ *             (bit 1 -> +1); the caller draws them
+ *   U_bits    (device) out: device layout, M x rp signs (u_j is column j)
+ *   V_bits    (device) out: device layout, rp x N signs (v_j is row j)
+ *   alpha_r_f16 (device) out: fp16 [rp], the refitted coefficients
+ *   alpha, alpha_greedy (host, optional) out: fp64 [r]
+ *   sse       (host, optional) out: [0] = ||R||^2 after the greedy pass,
+ *             [1] = the squared error with the refitted coefficients
+ *             (from ||W||^2 - 2 alpha.c + alpha^T G alpha)
+ *   solved    (host, optional) out: 1 if the refit was solved, else 0
+ *   workspace (device, 256-byte aligned) >= binlr_fit_workspace_bytes(M, N, r)
+ *             (8 M N bytes of fp64 residual plus O(r^2 + M r + N r))
+ * rp = r rounded up to a multiple of 32; the padding components are u = v =
+ * +1 with coefficient 0, so U_bits, V_bits, alpha_r_f16 and rp go straight
+ * to binlr_apply / bsg_linear.  1 <= r <= 2048, 1 <= rounds <= 64,
+ * N % 32 == 0.  Offline: the call synchronises the stream (the r x r system
+ * is solved on the host) and returns when the outputs are written.
+ */
+BSG_API size_t binlr_fit_workspace_bytes(int M, int N, int r);
+BSG_API bsg_status binlr_fit(const float* W, int M, int N, int r, int rounds, const uint32_t* v_init,
+                             uint32_t* U_bits, uint32_t* V_bits, uint16_t* alpha_r_f16, double* alpha,
+                             double* alpha_greedy, double* sse, int* solved, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * bsg_linear -- the whole layer in one pass over x: the binary bases
  * (FluxBin Sec. 3.1/3.2), the binary low-rank correction (BiLoCo "The core
  * idea") and the protected int8 rows (BiSCo-LLM "Sensitivity Protection"):

@@ -144,6 +144,41 @@ def test_bs_gemv_multi_validation():
     assert _multi([(None, None, None, None, 0)]) == OK   # empty outputs: a no-op
 
 
+def _fit(W=A16, M=64, N=64, r=8, rounds=5, v0=A16b, U=A16c, V=A16d, a16=A16, ws=A16b, nb=None):
+    if nb is None:
+        nb = bsg.lib().binlr_fit_workspace_bytes(M, N, r) if r > 0 and N % 32 == 0 and M > 0 else 0
+    return bsg.lib().binlr_fit(W, M, N, r, rounds, v0, U, V, a16, None, None, None, None, ws, nb, None)
+
+
+def test_binlr_fit_workspace_bytes():
+    nb = bsg.lib().binlr_fit_workspace_bytes(5120, 5120, 512)
+    assert nb >= 8 * 5120 * 5120                 # the fp64 residual
+    assert nb < 8 * 5120 * 5120 + (64 << 20)
+    assert bsg.lib().binlr_fit_workspace_bytes(64, 33, 8) == 0
+    assert bsg.lib().binlr_fit_workspace_bytes(64, 64, 0) == 0
+    assert bsg.lib().binlr_fit_workspace_bytes(64, 64, 2049) == 0
+
+
+@fake_ptrs
+def test_binlr_fit_validation():
+    assert _fit(M=0) == ESHAPE
+    assert _fit(N=33) == ESHAPE
+    assert _fit(r=0) == ESHAPE
+    assert _fit(r=2049) == ESHAPE
+    assert _fit(rounds=0) == ESHAPE
+    assert _fit(rounds=65) == ESHAPE
+    assert _fit(W=None) == ENULL
+    assert _fit(v0=None) == ENULL
+    assert _fit(U=None) == ENULL
+    assert _fit(V=None) == ENULL
+    assert _fit(a16=None) == ENULL
+    assert _fit(W=A16 + 2) == EALIGN
+    assert _fit(U=A16c + 4) == EALIGN
+    assert _fit(ws=A16b + 16) == EALIGN
+    assert _fit(ws=None) == EWS
+    assert _fit(nb=100) == EWS
+
+
 @fake_ptrs
 def test_bs_gemv_i8_validation():
     L = bsg.lib()
