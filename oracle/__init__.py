@@ -65,6 +65,8 @@ def lib():
             "or_logical_to_layout": (None, [_P, _I, _I, _I, _P]),
             "or_layout_to_logical": (None, [_P, _I, _I, _I, _P]),
             "or_binlr_fit": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+            "or_pack_grouped": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P]),
+            "or_sign_gemv_grouped": (None, [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -232,6 +234,37 @@ def salient_select(W, xbar, ns: int, alpha=None):
 
 
 # ---------------------------------------------------------------- layout
+def pack_grouped(W, K: int, g: int, with_colscale: bool = False):
+    """Greedy residual bases with one row scale per group of g columns (FluxBin Sec. 3.1); see
+    or_pack_grouped.  Returns (bits [K][M][ceil(N/32)], alpha fp32 [K][M][N/g], colscale fp16 bits [K][N]
+    or None)."""
+    W = _c(np.asarray(W, np.float32), np.float32)
+    M, N = W.shape
+    bits = np.zeros((K, M, words(N)), np.uint32)
+    alpha = np.zeros((K, M, N // g), np.float32)
+    cs = np.zeros((K, N), np.uint16) if with_colscale else None
+    rc = lib().or_pack_grouped(_ptr(W), M, N, K, g, 1 if with_colscale else 0, _ptr(bits), _ptr(alpha), _ptr(cs))
+    if rc != 0:
+        raise ValueError("pack_grouped failed (%d)" % rc)
+    return bits, alpha, cs
+
+
+def sign_gemv_grouped(bits, K, M, N, g, alpha, x, colscale_f16=None) -> np.ndarray:
+    """y [M][B] in float64 for group-wise row scales alpha fp32 [K][M][N/g]."""
+    x = np.asarray(x, np.float64)
+    if x.ndim == 1:
+        x = x[:, None]
+    B = x.shape[1]
+    bits = _c(bits, np.uint32).reshape(-1)
+    a = _c(np.asarray(alpha, np.float32), np.float32).reshape(-1)
+    assert a.size == K * M * (N // g)
+    cs = None if colscale_f16 is None else _c(np.asarray(colscale_f16, np.uint16), np.uint16).reshape(-1)
+    xc = _c(x, np.float64)
+    y = np.zeros((M, B), np.float64)
+    lib().or_sign_gemv_grouped(_ptr(bits), K, M, N, g, _ptr(a), _ptr(cs), _ptr(xc), B, _ptr(y))
+    return y
+
+
 def binlr_fit(W, r: int, vinit, rounds: int = 5):
     """Offline binary low-rank fit (BiLoCo "Finding the sign vectors", "Joint
     refit"); see or_binlr_fit.  W: fp32 [M][N] (any N > 0); vinit: logical

@@ -441,6 +441,102 @@ OR_API void or_layout_to_logical(const uint32_t* phys, int K, int M, int N, uint
         logical[((size_t)k * M + m) * nd + w] = phys[or_layout_offset(K, M, N, k, m, (int)w)];
 }
 
+/*
+ * Group-wise row scales [FluxBin Sec. 3.1: one row scale per weight group;
+ * Sec. 4 setup: group size g = 128 in the Kb-g128 configurations].  The
+ * greedy residual recipe of or_pack with the row scale taken per row and
+ * per group of g consecutive columns (g divides N; g = N is or_pack):
+ *   alpha_k[m][j] = fp32( sum_{n in group j} |R[m,n]| / g )
+ *   if colscale: c_k[n] = fp16(fp32( num_n / den_j )),
+ *                num_n = sum_m alpha_k[m][j] |R[m,n]|, den_j = sum_m
+ *                alpha_k[m][j]^2 for the group j of column n (least squares
+ *                given the group scales; c = 1 when den_j == 0), else c = 1
+ *   R <- R - alpha_k[m][j(n)] * c_k[n] * B_k[m,n]
+ * alpha is fp32 [K][M][N/g].  Returns 0, -1 on bad sizes or allocation
+ * failure, -2 on a NaN in W.
+ */
+OR_API int or_pack_grouped(const float* W, int M, int N, int K, int g, int with_colscale,
+                           uint32_t* bits, float* alpha, uint16_t* colscale) {
+  if (g <= 0 || N % g != 0) return -1;
+  const int nd = (N + 31) / 32, G = N / g;
+  const size_t mn = (size_t)M * N;
+  double* R = (double*)malloc(sizeof(double) * (mn ? mn : 1));
+  double* cdbl = (double*)malloc(sizeof(double) * (N > 0 ? N : 1));
+  if (!R || !cdbl) { free(R); free(cdbl); return -1; }
+  for (size_t i = 0; i < mn; ++i) {
+    if (isnan(W[i])) { free(R); free(cdbl); return -2; }
+    R[i] = (double)W[i];
+  }
+  memset(bits, 0, sizeof(uint32_t) * (size_t)K * M * nd);
+  for (int k = 0; k < K; ++k) {
+    uint32_t* bk = bits + (size_t)k * M * nd;
+    float* ak = alpha + (size_t)k * M * G;   /* ak[m * G + j] */
+    for (int m = 0; m < M; ++m)
+      for (int n = 0; n < N; ++n)
+        if (R[(size_t)m * N + n] >= 0.0) bk[(size_t)m * nd + (n >> 5)] |= 1u << (n & 31);
+    for (int m = 0; m < M; ++m)
+      for (int j = 0; j < G; ++j) {
+        double s = 0.0;
+        for (int n = j * g; n < (j + 1) * g; ++n) s += fabs(R[(size_t)m * N + n]);
+        ak[(size_t)m * G + j] = (float)(s / (double)g);
+      }
+    for (int n = 0; n < N; ++n) cdbl[n] = 1.0;
+    if (with_colscale) {
+      for (int j = 0; j < G; ++j) {
+        double den = 0.0;
+        for (int m = 0; m < M; ++m) den += (double)ak[(size_t)m * G + j] * (double)ak[(size_t)m * G + j];
+        for (int n = j * g; n < (j + 1) * g; ++n) {
+          uint16_t h;
+          if (den == 0.0) {
+            h = 0x3c00u;
+          } else {
+            double num = 0.0;
+            for (int m = 0; m < M; ++m) num += (double)ak[(size_t)m * G + j] * fabs(R[(size_t)m * N + n]);
+            h = or_f32_to_f16((float)(num / den));
+          }
+          colscale[(size_t)k * N + n] = h;
+          cdbl[n] = or_f16_to_f64(h);
+        }
+      }
+    }
+    for (int m = 0; m < M; ++m)
+      for (int n = 0; n < N; ++n) {
+        double sgn = (bk[(size_t)m * nd + (n >> 5)] >> (n & 31)) & 1u ? 1.0 : -1.0;
+        double t = (double)ak[(size_t)m * G + n / g] * cdbl[n];
+        R[(size_t)m * N + n] = R[(size_t)m * N + n] - t * sgn;
+      }
+  }
+  free(cdbl);
+  free(R);
+  return 0;
+}
+
+/*
+ * The product with group-wise row scales [FluxBin Sec. 3.1]:
+ *   y[m,b] = sum_k sum_j alpha_k[m][j] sum_{n in group j} (2 bit_k(m,n) - 1) c_k[n] x[n,b]
+ * alpha fp32 [K][M][N/g]; colscale fp16 bits [K][N] or NULL; x [N][B]
+ * (double); y [M][B] double.  Sums in double, ascending order.
+ */
+OR_API void or_sign_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, const float* alpha,
+                                 const uint16_t* colscale, const double* x, int B, double* y) {
+  const int nd = (N + 31) / 32, G = N / g;
+  for (int m = 0; m < M; ++m)
+    for (int b = 0; b < B; ++b) {
+      double tot = 0.0;
+      for (int k = 0; k < K; ++k)
+        for (int j = 0; j < G; ++j) {
+          double acc = 0.0;
+          for (int n = j * g; n < (j + 1) * g; ++n) {
+            const int bit = (bits[((size_t)k * M + m) * nd + (n >> 5)] >> (n & 31)) & 1u;
+            const double c = colscale ? or_f16_to_f64(colscale[(size_t)k * N + n]) : 1.0;
+            acc += (bit ? 1.0 : -1.0) * c * x[(size_t)n * B + b];
+          }
+          tot += (double)alpha[((size_t)k * M + m) * G + j] * acc;
+        }
+      y[(size_t)m * B + b] = tot;
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Offline fit of the binary low-rank correction.                       */
 /* ------------------------------------------------------------------ */

@@ -569,3 +569,85 @@ def test_lr_fit_singular_refit_keeps_the_greedy_coefficients():
     np.testing.assert_array_equal(ag, [0.5, 0.0])
     np.testing.assert_array_equal(al, ag)
     assert sse_g == 0.0 and sse_r == 0.0
+
+
+# ----------------------------------------------------------- group-wise row scales
+@pytest.mark.parametrize("cs", [False, True])
+def test_grouped_pack_with_one_group_is_the_row_scale_pack(cs):
+    """g = N: one group per row, the recipe of or_pack (bits, scales bit for bit)."""
+    M, N, K = 12, 96, 2
+    W = synth.weights(61, 0, M, N)
+    b1, a1, c1 = oracle.pack(W, K, cs)
+    b2, a2, c2 = oracle.pack_grouped(W, K, N, cs)
+    np.testing.assert_array_equal(b1, b2)
+    np.testing.assert_array_equal(a1.view(np.uint32), a2[:, :, 0].view(np.uint32))
+    if cs:
+        np.testing.assert_array_equal(c1, c2)
+    x = synth.random_x(61, N, 2, "f32")
+    np.testing.assert_array_equal(oracle.sign_gemv(b1, K, M, N, a1, x, c1),
+                                  oracle.sign_gemv_grouped(b2, K, M, N, N, a2, x, c2))
+
+
+@pytest.mark.parametrize("cs", [False, True])
+def test_grouped_product_equals_the_dense_dequantised_matmul(cs):
+    M, N, K, g = 9, 256, 2, 64
+    W = synth.weights(62, 0, M, N)
+    bits, alpha, csb = oracle.pack_grouped(W, K, g, cs)
+    S = _dense_signs(bits, K, M, N)
+    c = oracle.f16_to_f64(csb).reshape(K, N) if cs else np.ones((K, N))
+    a = np.repeat(alpha.astype(np.float64), g, axis=2)          # [K][M][N]: the scale of each entry's group
+    What = (a * c[:, None, :] * S).sum(0)
+    x = synth.random_x(62, N, 3, "f32").astype(np.float64)
+    np.testing.assert_allclose(oracle.sign_gemv_grouped(bits, K, M, N, g, alpha, x, csb), What @ x,
+                               rtol=1e-12, atol=1e-15)
+
+
+def test_grouped_alpha_is_the_fp32_argmin_per_group():
+    """Moving a group scale by one fp32 ulp either way never lowers that
+    group's error (exact rationals)."""
+    M, N, g = 4, 96, 32
+    W = synth.weights(63, 0, M, N)
+    bits, alpha, _ = oracle.pack_grouped(W, 1, g, False)
+    S = _dense_signs(bits, 1, M, N)[0]
+    for m in range(M):
+        for j in range(N // g):
+            R = [Fraction(float(v)) for v in W[m, j * g:(j + 1) * g]]
+            sg = [int(v) for v in S[m, j * g:(j + 1) * g]]
+
+            def sse(a):
+                a = Fraction(float(a))
+                return sum((r - a * si) ** 2 for r, si in zip(R, sg))
+
+            a0 = alpha[0, m, j]
+            base = sse(a0)
+            for d in (np.inf, -np.inf):
+                assert sse(np.nextafter(a0, np.float32(d))) >= base
+
+
+def test_grouped_colscale_is_the_least_squares_value_per_group():
+    """c[n] = fp16(fp32(sum_m alpha[m][j] |R| / sum_m alpha[m][j]^2)) with the
+    group j of column n, written out in exact rationals for the first base."""
+    M, N, g = 5, 64, 32
+    W = synth.weights(64, 0, M, N)
+    bits, alpha, cs = oracle.pack_grouped(W, 1, g, True)
+    for n in range(N):
+        j = n // g
+        num = sum(Fraction(float(alpha[0, m, j])) * abs(Fraction(float(W[m, n]))) for m in range(M))
+        den = sum(Fraction(float(alpha[0, m, j])) ** 2 for m in range(M))
+        want = oracle.f32_to_f16(np.array([np.float32(float(num / den))], np.float32))[0]
+        assert cs[0, n] == want
+
+
+def test_grouped_scales_never_fit_worse_than_row_scales():
+    """Same signs, scales fitted per group instead of per row: the error of
+    the first base cannot grow (each group scale is optimal on its group)."""
+    M, N = 16, 512
+    W = synth.weights(65, 0, M, N)
+    Wd = W.astype(np.float64)
+    b1, a1, _ = oracle.pack(W, 1, False)
+    b2, a2, _ = oracle.pack_grouped(W, 1, 128, False)
+    np.testing.assert_array_equal(b1, b2)
+    S = _dense_signs(b1, 1, M, N)[0]
+    e_row = ((Wd - a1[0].astype(np.float64)[:, None] * S) ** 2).sum()
+    e_grp = ((Wd - np.repeat(a2[0].astype(np.float64), 128, axis=1) * S) ** 2).sum()
+    assert e_grp <= e_row * (1 + 1e-7)
