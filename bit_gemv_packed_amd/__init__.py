@@ -56,6 +56,9 @@ _SIGS = {
     "bs_gemv": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P]),
     "bs_gemv_i8": (ctypes.c_int32, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _I, _P]),
     "bs_gemv_multi": (ctypes.c_int32, [_P, _I, _I, _I, _P, _I, _I, _I, _P]),
+    "bsq_pack_grouped_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "bsq_pack_grouped": (ctypes.c_int32, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "bs_gemv_grouped": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P]),
     "binlr_fit_workspace_bytes": (_SZ, [_I, _I, _I]),
     "binlr_fit": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "binlr_apply": (ctypes.c_int32, [_P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P, _SZ, _P]),
@@ -199,6 +202,35 @@ def bsq_pack(W, K: int, colscale: bool = False, workspace=None):
     _check("bsq_pack", lib().bsq_pack(_ptr(W), M, N, K, BSG_PACK_COLSCALE if colscale else 0, _ptr(bits),
                                       _ptr(alpha), _ptr(cs), ws.data_ptr(), ws.numel(), _stream(dev)))
     return bits, alpha, cs
+
+
+def bsq_pack_grouped(W, K: int, g: int, colscale: bool = False, workspace=None):
+    """bsq_pack with one row scale per group of g columns.  Returns (bits, alpha fp32 [K][M][N/g],
+    colscale fp16-bits int16 [K][N] or None)."""
+    torch = _torch()
+    M, N = W.shape
+    dev = W.device
+    bits = torch.empty(layout_words(K, M, N), dtype=torch.int32, device=dev)
+    alpha = torch.empty((K, M, max(1, N // g)), dtype=torch.float32, device=dev)
+    cs = torch.empty((K, N), dtype=torch.int16, device=dev) if colscale else None
+    nb = int(lib().bsq_pack_grouped_workspace_bytes(M, N, g))
+    ws = workspace if workspace is not None else torch.empty(max(1, nb), dtype=torch.uint8, device=dev)
+    _check("bsq_pack_grouped", lib().bsq_pack_grouped(_ptr(W), M, N, K, g, BSG_PACK_COLSCALE if colscale else 0,
+                                                      _ptr(bits), _ptr(alpha), _ptr(cs), ws.data_ptr(), ws.numel(),
+                                                      _stream(dev)))
+    return bits, alpha, cs
+
+
+def bs_gemv_grouped(bits, K: int, M: int, N: int, g: int, alpha, x, colscale=None, y=None, accumulate: bool = False):
+    """y (fp32 [M][B]) = or += the product with group-wise row scales alpha fp32 [K][M][N/g]."""
+    torch = _torch()
+    B = _xshape(x, N)
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, B), dtype=torch.float32, device=dev)
+    _check("bs_gemv_grouped", lib().bs_gemv_grouped(_ptr(bits), K, M, N, g, _ptr(alpha), _ptr(colscale), _ptr(x),
+                                                    _dtype_code(x), B, _ptr(y), 1 if accumulate else 0, _stream(dev)))
+    return y
 
 
 def bsq_pack_signs(S):

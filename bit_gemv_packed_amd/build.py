@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "bsg")
 LIB = os.path.join(HERE, "libbsg.so")
 SOURCES = ["bsg_abi.hip", "bsg_gemv.hip", "bsg_gemv_mfma.hip", "bsg_gemv_i8.hip", "bsg_pack.hip", "bsg_misc.hip",
-           "bsg_lrfit.hip"]
+           "bsg_lrfit.hip", "bsg_gemv_gs.hip"]
 ARCH = os.environ.get("BSG_OFFLOAD_ARCH", "gfx950")
 
 CFLAGS = [
@@ -46,7 +46,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(7, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]

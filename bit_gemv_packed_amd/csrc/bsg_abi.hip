@@ -10,6 +10,8 @@ namespace bsg {
 hipError_t launch_pack(const float* W, int M, int N, int K, bool colscale, uint32_t* bits, float* alpha,
                        uint16_t* cs, void* ws, hipStream_t st);
 hipError_t launch_pack_signs(const float* S, int M, int N, uint32_t* bits, hipStream_t st);
+hipError_t launch_pack_grouped(const float* W, int M, int N, int K, int g, bool colscale, uint32_t* bits,
+                               float* alpha, uint16_t* cs, void* ws, hipStream_t st);
 hipError_t launch_absmean(const float* X, int S, int N, float* xbar, hipStream_t st);
 hipError_t launch_salient(const float* W, int M, int N, const float* xbar, int ns, int32_t* rows, int8_t* q,
                           uint16_t* s, float* alpha, int K, void* ws, hipStream_t st);
@@ -264,6 +266,61 @@ bsg_status bs_gemv_multi(const bsg_proj* projs, int P, int K, int N, const void*
   }
   a.np = np;
   return hip_status(launch_prod_multi(a, st));
+}
+
+// group size: a power of two >= 64 dividing N
+static bool bad_group(int N, int g) { return g < 64 || (g & (g - 1)) != 0 || N % g != 0; }
+
+size_t bsq_pack_grouped_workspace_bytes(int M, int N, int g) {
+  if (M < 0 || bad_n(N) || bad_group(N, g)) return 0;
+  return align_up((size_t)M * N * 8, 256) + align_up((size_t)(N / g) * 8, 256);
+}
+
+bsg_status bsq_pack_grouped(const float* W, int M, int N, int K, int g, int flags, uint32_t* bits, float* alpha,
+                            uint16_t* colscale, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool cs = (flags & BSG_PACK_COLSCALE) != 0;
+  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || bad_group(N, g) || (flags & ~BSG_PACK_COLSCALE))
+    return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!W || !bits || !alpha || (cs && !colscale)) return BSG_ERR_NULL;
+  if (misaligned(W, 4) || misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(colscale, 2) ||
+      misaligned(workspace, 16))
+    return BSG_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bsq_pack_grouped_workspace_bytes(M, N, g)) return BSG_ERR_WORKSPACE;
+  return hip_status(launch_pack_grouped(W, M, N, K, g, cs, bits, alpha, cs ? colscale : nullptr, workspace,
+                                        (hipStream_t)stream));
+}
+
+bsg_status bs_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, const float* alpha,
+                           const uint16_t* colscale, const void* x, int x_dtype, int B, float* y, int accumulate,
+                           void* stream) {
+  if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
+  if (K < 1 || K > 4 || M < 0 || bad_n(N) || bad_group(N, g) || B < 1 || B > kMaxB ||
+      too_big(K, M, N, B) || (size_t)K * M * (N / g) >= (1u << 30))
+    return BSG_ERR_SHAPE;
+  if (M == 0) return BSG_OK;
+  if (!bits || !alpha || !x || !y) return BSG_ERR_NULL;
+  if (misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(colscale, 2) ||
+      misaligned(x, dtype_size(x_dtype)) || misaligned(y, 4))
+    return BSG_ERR_ALIGN;
+  ProdArgs a{};
+  a.bits = bits;
+  a.alpha = alpha;
+  a.colscale = colscale;
+  a.x = x;
+  a.y = y;
+  a.plane = plane_words(M, N / 32);
+  a.K = K;
+  a.M = M;
+  a.N = N;
+  a.ND = N / 32;
+  a.B = B;
+  a.xdt = x_dtype;
+  a.accumulate = accumulate ? 1 : 0;
+  a.xvec = xvec_ok(x, colscale);
+  a.gsw = g / 32;
+  a.ngrp = N / g;
+  return hip_status(launch_prod_grouped(a, (hipStream_t)stream));
 }
 
 size_t binlr_fit_workspace_bytes(int M, int N, int r) {

@@ -1,0 +1,51 @@
+// Binary-base product with group-wise row scales (FluxBin Sec. 3.1: one row
+// scale per weight group; g = 128 in its Kb-g128 configurations):
+//
+//   y[m,b] (= or +=) sum_k sum_j alpha_k[m][j] sum_{n in group j} (2 bit_k(m,n) - 1) c_k[n] x[n,b]
+//
+// The table kernel of bsg_prod_f.h with GS = 1: every lane sums its words of
+// a chunk apart (they lie in one group) and adds that sum times its group's
+// scale.  One batch column per launch.
+#include "bsg_prod_f.h"
+
+namespace bsg {
+
+// Every (Q, NWL, KM) the grouped planner may choose (K <= 4, one batch
+// column, NWL <= the words of a group).
+#define BSG_PROD_GS_INSTANCES(X)                                                                              \
+  BSG_PROD_XM(X, 4, 2, 1) BSG_PROD_XM(X, 4, 2, 2) BSG_PROD_XM(X, 2, 4, 1) BSG_PROD_XM(X, 2, 4, 2)            \
+  BSG_PROD_XM(X, 1, 8, 1) BSG_PROD_XM(X, 1, 8, 2) BSG_PROD_XM(X, 4, 2, 3) BSG_PROD_XM(X, 4, 2, 4)            \
+  BSG_PROD_XM(X, 2, 4, 3) BSG_PROD_XM(X, 2, 4, 4) BSG_PROD_XM(X, 4, 1, 3) BSG_PROD_XM(X, 4, 1, 4)            \
+  BSG_PROD_XM(X, 2, 2, 3) BSG_PROD_XM(X, 2, 2, 4) BSG_PROD_XM(X, 1, 4, 3) BSG_PROD_XM(X, 1, 4, 4)
+
+static hipError_t dispatch_gs(const ProdArgs& a, const ProdPlan& p, hipStream_t st) {
+  switch (prod_key(p.Q, p.NWL, p.KM, p.BB, p.XM)) {
+#define BSG_CASE(Q, NWL, KM, BB, XM) \
+  case prod_key(Q, NWL, KM, BB, XM): return launch_one(k_prod_f<Q, NWL, KM, BB, XM, 0, 1>, p, a, st);
+    BSG_PROD_GS_INSTANCES(BSG_CASE)
+#undef BSG_CASE
+    default: return hipErrorInvalidConfiguration;
+  }
+}
+
+hipError_t launch_prod_grouped(const ProdArgs& a0, hipStream_t st) {
+  ProdPlan p = plan_prod(a0.K, a0.M, a0.N, a0.B, a0.colscale != nullptr, false, a0.gsw);
+  if (p.KM > 4 || p.BB != 1) return hipErrorInvalidConfiguration;
+  ProdArgs as = a0;
+  as.x_bytes = (uint32_t)((size_t)a0.N * a0.B * (a0.xdt == BSG_F32 ? 4 : 2));
+  as.cs_bytes = a0.colscale ? (uint32_t)((size_t)a0.K * a0.N * 2) : 0u;
+  as.al_bytes = (uint32_t)((size_t)a0.K * a0.M * a0.ngrp * 4);
+  p.XM = (a0.B == 1 && a0.xvec && a0.xdt != BSG_F32) ? (a0.xdt == BSG_BF16 ? 1 : 2) : 0;
+  for (int c = 0; c < p.nlaunch; ++c) {
+    ProdArgs a = as;
+    a.b0 = c;
+    a.W = p.W;
+    a.NCH = p.NCH;
+    a.wave_lds = (uint32_t)p.wave_lds;
+    const hipError_t e = dispatch_gs(a, p, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace bsg

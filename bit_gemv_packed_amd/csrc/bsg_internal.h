@@ -68,7 +68,9 @@ struct ProdPlan {
   size_t lds;       // LDS bytes per workgroup
 };
 
-ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool int8_mode);
+// gsw > 0: group-wise row scales with groups of gsw sign words (one batch
+// column per launch, lanes kept inside a group).
+ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool int8_mode, int gsw = 0);
 
 // One projection of a fused launch (bs_gemv_multi): its own weights, scales
 // and output, the first workgroup of its row blocks in the grid.
@@ -100,6 +102,7 @@ struct ProdArgs {
   // that the kernel prologue has no branches
   uint32_t x_bytes, cs_bytes, al_bytes;
   int xvec;                  // x 16-byte and colscale 8-byte aligned: vector loads
+  int gsw, ngrp;             // group-wise row scales: sign words per group, groups per row
   // int8 path
   const int8_t* xq;          // [N][B]
   const float* sx;           // [B]
@@ -125,6 +128,8 @@ struct ProdArgs {
 hipError_t launch_prod_f(const ProdArgs& a, const ProdPlan& p, hipStream_t s);
 // One launch over a.np > 1 projections (a.proj) sharing x (bsg_gemv.hip).
 hipError_t launch_prod_multi(const ProdArgs& a, hipStream_t s);
+// Group-wise row scales (bsg_gemv_gs.hip): a.gsw, a.ngrp set, alpha [K][M][ngrp].
+hipError_t launch_prod_grouped(const ProdArgs& a, hipStream_t s);
 // Batched product on the matrix cores (bsg_gemv_mfma.hip): B >= 4 columns of
 // bf16 / fp16 x, no column scales.
 bool mfma_eligible(int B, int xdt, bool colscale);

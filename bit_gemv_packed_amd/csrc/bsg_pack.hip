@@ -23,10 +23,12 @@ __global__ void k_widen(const float* __restrict__ W, double* __restrict__ R, siz
 
 // mode 0: out[m] = fp32(sum_n |R[m,n]| / N)                (row scale)
 // mode 1: outd[m] = sum_n |W[m,n]| * xbar[n]  (W fp32)      (protected-row score)
+// mode 2: out[m * (N / g) + j] = fp32(sum_{n in group j} |R[m,n]| / g)
+//         (group-wise row scales; g a multiple of the 64-column tile)
 template <int MODE>
 __global__ void __launch_bounds__(kT) k_rowsum(const double* __restrict__ R, const float* __restrict__ W,
                                               const float* __restrict__ xbar, int M, int N,
-                                              float* __restrict__ out, double* __restrict__ outd) {
+                                              float* __restrict__ out, double* __restrict__ outd, int g) {
   __shared__ double tile[kT][kT + 1];
   const int t = threadIdx.x;
   const int m0 = blockIdx.x * kT;
@@ -37,7 +39,7 @@ __global__ void __launch_bounds__(kT) k_rowsum(const double* __restrict__ R, con
       const int m = m0 + i;
       double v = 0.0;
       if (m < M && n < N) {
-        if (MODE == 0) {
+        if (MODE != 1) {
           v = fabs(R[(size_t)m * N + n]);
         } else {
           v = fabs((double)W[(size_t)m * N + n]) * (double)xbar[n];
@@ -49,11 +51,16 @@ __global__ void __launch_bounds__(kT) k_rowsum(const double* __restrict__ R, con
     const int lim = min(kT, N - n0);
     for (int j = 0; j < lim; ++j) acc = acc + tile[t][j];
     __syncthreads();
+    if (MODE == 2 && (n0 + kT) % g == 0) {  // end of group (n0 + kT) / g - 1
+      const int m = m0 + t;
+      if (m < M) out[(size_t)m * (N / g) + (n0 + kT) / g - 1] = (float)(acc / (double)g);
+      acc = 0.0;
+    }
   }
   const int m = m0 + t;
   if (m < M) {
     if (MODE == 0) out[m] = (float)(acc / (double)N);
-    else outd[m] = acc;
+    else if (MODE == 1) outd[m] = acc;
   }
 }
 
@@ -114,6 +121,51 @@ __global__ void k_residual(double* __restrict__ R, const float* __restrict__ alp
     const double sgn = r >= 0.0 ? 1.0 : -1.0;
     const double c = cs ? (double)f16_bits_to_float(cs[n]) : 1.0;
     const double t = (double)alpha[m] * c;
+    R[i] = r - t * sgn;
+  }
+}
+
+// Group-wise row scales alpha [M][G] (G = N / g): den[j] = sum_m alpha[m][j]^2,
+// cs[n] = fp16(fp32(sum_m alpha[m][j] |R[m,n]| / den[j])) for the group j of
+// n (1 when den[j] == 0), and the residual update with alpha[m][j(n)].
+__global__ void k_den_grouped(const float* __restrict__ alpha, int M, int G, double* __restrict__ den) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= G) return;
+  double s = 0.0;
+  for (int m = 0; m < M; ++m) s = s + (double)alpha[(size_t)m * G + j] * (double)alpha[(size_t)m * G + j];
+  den[j] = s;
+}
+
+__global__ void k_colscale_grouped(const double* __restrict__ R, const float* __restrict__ alpha,
+                                   const double* __restrict__ den, int M, int N, int g, uint16_t* __restrict__ cs) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const int G = N / g, j = n / g;
+  const double d = den[j];
+  uint16_t h;
+  if (d == 0.0) {
+    h = 0x3c00u;
+  } else {
+    double num = 0.0;
+    for (int m = 0; m < M; ++m) num = num + (double)alpha[(size_t)m * G + j] * fabs(R[(size_t)m * N + n]);
+    const float c32 = (float)(num / d);
+    const _Float16 c16 = (_Float16)c32;
+    __builtin_memcpy(&h, &c16, 2);
+  }
+  cs[n] = h;
+}
+
+__global__ void k_residual_grouped(double* __restrict__ R, const float* __restrict__ alpha,
+                                   const uint16_t* __restrict__ cs, int M, int N, int g) {
+  const size_t total = (size_t)M * N;
+  const int G = N / g;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i / N);
+    const int n = (int)(i % N);
+    const double r = R[i];
+    const double sgn = r >= 0.0 ? 1.0 : -1.0;
+    const double c = cs ? (double)f16_bits_to_float(cs[n]) : 1.0;
+    const double t = (double)alpha[(size_t)m * G + n / g] * c;
     R[i] = r - t * sgn;
   }
 }
@@ -230,12 +282,38 @@ hipError_t launch_pack(const float* W, int M, int N, int K, bool colscale, uint3
     uint16_t* ck = colscale ? cs + (size_t)k * N : nullptr;
     hipLaunchKernelGGL(k_signs<double>, dim3(pad_rows(M)), dim3(64), 0, st, R, M, N, bits, plane, k);
     hipLaunchKernelGGL(k_rowsum<0>, dim3((M + kT - 1) / kT), dim3(kT), 0, st, R, (const float*)nullptr,
-                       (const float*)nullptr, M, N, ak, (double*)nullptr);
+                       (const float*)nullptr, M, N, ak, (double*)nullptr, 0);
     if (colscale) {
       hipLaunchKernelGGL(k_den, dim3(1), dim3(64), 0, st, ak, M, den);
       hipLaunchKernelGGL(k_colscale, dim3((N + 255) / 256), dim3(256), 0, st, R, ak, den, M, N, ck);
     }
     if (k + 1 < K) hipLaunchKernelGGL(k_residual, dim3(grid_for(mn, 256)), dim3(256), 0, st, R, ak, ck, M, N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_pack_grouped(const float* W, int M, int N, int K, int g, bool colscale, uint32_t* bits,
+                               float* alpha, uint16_t* cs, void* ws, hipStream_t st) {
+  double* R = (double*)ws;
+  double* den = (double*)((char*)ws + align_up((size_t)M * N * 8, 256));
+  const size_t mn = (size_t)M * N;
+  const int ND = N / 32, G = N / g;
+  const size_t plane = plane_words(M, ND);
+  hipLaunchKernelGGL(k_widen, dim3(grid_for(mn, 256)), dim3(256), 0, st, W, R, mn);
+  for (int k = 0; k < K; ++k) {
+    float* ak = alpha + (size_t)k * M * G;
+    uint16_t* ck = colscale ? cs + (size_t)k * N : nullptr;
+    hipLaunchKernelGGL(k_signs<double>, dim3(pad_rows(M)), dim3(64), 0, st, R, M, N, bits, plane, k);
+    hipLaunchKernelGGL(k_rowsum<2>, dim3((M + kT - 1) / kT), dim3(kT), 0, st, R, (const float*)nullptr,
+                       (const float*)nullptr, M, N, ak, (double*)nullptr, g);
+    if (colscale) {
+      hipLaunchKernelGGL(k_den_grouped, dim3((G + 255) / 256), dim3(256), 0, st, ak, M, G, den);
+      hipLaunchKernelGGL(k_colscale_grouped, dim3((N + 255) / 256), dim3(256), 0, st, R, ak, den, M, N, g, ck);
+    }
+    if (k + 1 < K)
+      hipLaunchKernelGGL(k_residual_grouped, dim3(grid_for(mn, 256)), dim3(256), 0, st, R, ak, ck, M, N, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -257,7 +335,7 @@ hipError_t launch_salient(const float* W, int M, int N, const float* xbar, int n
   double* score = (double*)ws;
   int* sel = (int*)((char*)ws + align_up((size_t)M * 8, 256));
   hipLaunchKernelGGL(k_rowsum<1>, dim3((M + kT - 1) / kT), dim3(kT), 0, st, (const double*)nullptr, W, xbar, M, N,
-                     (float*)nullptr, score);
+                     (float*)nullptr, score, 0);
   hipLaunchKernelGGL(k_rank, dim3((M + 255) / 256), dim3(256), 0, st, score, M, ns, sel);
   hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, sel, M, ns, rows);
   if (ns > 0) hipLaunchKernelGGL(k_quant_rows, dim3(ns), dim3(256), 0, st, W, M, N, rows, q, s, alpha, K);

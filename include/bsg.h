@@ -218,6 +218,40 @@ BSG_API bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const floa
                    float* y, int accumulate, void* stream);
 
 /*
+ * bsq_pack_grouped -- bsq_pack with one row scale per row and per group of g
+ * consecutive columns (FluxBin Sec. 3.1: a row scale per weight group;
+ * g = 128 in its Kb-g128 configurations):
+ *   alpha_k[m][j] = fp32( sum_{n in group j} |R[m,n]| / g )
+ *   c_k[n] = fp16(fp32( sum_m alpha_k[m][j] |R[m,n]| / sum_m alpha_k[m][j]^2 ))
+ *            for the group j of column n (BSG_PACK_COLSCALE; 1 when the
+ *            denominator is 0)
+ *   R <- R - alpha_k[m][j(n)] c_k[n] B_k[m,n]
+ *   alpha     (device) out: fp32 [K][M][N/g]
+ *   other arguments as bsq_pack; workspace >= bsq_pack_grouped_workspace_bytes.
+ * g a power of two >= 64 dividing N (N % 32 == 0).  g = N gives bsq_pack's
+ * result.  fp64 sums in ascending order: bit-exact with a sequential
+ * double-precision implementation of the recipe.
+ */
+BSG_API size_t bsq_pack_grouped_workspace_bytes(int M, int N, int g);
+BSG_API bsg_status bsq_pack_grouped(const float* W, int M, int N, int K, int g, int flags, uint32_t* bits,
+                                    float* alpha, uint16_t* colscale, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
+ * bs_gemv_grouped -- bs_gemv with group-wise row scales (FluxBin Sec. 3.1):
+ *   y[m,b] (= or +=) sum_k sum_j alpha[k][m][j] *
+ *                    sum_{n in group j} (2 bit_k(m,n) - 1) * c_k[n] * x[n,b]
+ *   alpha     (device) fp32 [K][M][N/g]
+ *   other arguments as bs_gemv.
+ * 1 <= K <= 4, g a power of two >= 64 dividing N, 1 <= B <= 64 (one launch
+ * per batch column).  fp32 sums in a fixed order, within
+ * 2e-3 * sum_k sum_j |alpha[k][m][j]| * sum_{n in j} |c_k[n] x[n,b]|.
+ */
+BSG_API bsg_status bs_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, const float* alpha,
+                                   const uint16_t* colscale, const void* x, int x_dtype, int B, float* y,
+                                   int accumulate, void* stream);
+
+/*
  * bs_gemv_multi -- several bs_gemv products that share x, in one launch
  * (projections that read the same activations, e.g. the query, key and
  * value projections, or the two projections of a gated MLP):

@@ -179,6 +179,34 @@ def test_binlr_fit_validation():
     assert _fit(nb=100) == EWS
 
 
+def _gg(bits=A16, K=2, M=128, N=256, g=128, alpha=A16b, cs=None, x=A16c, dt=2, B=1, y=A16d, acc=0):
+    return bsg.lib().bs_gemv_grouped(bits, K, M, N, g, alpha, cs, x, dt, B, y, acc, None)
+
+
+@fake_ptrs
+def test_grouped_validation():
+    assert _gg(dt=7) == EDTYPE
+    assert _gg(g=96) == ESHAPE          # not a power of two
+    assert _gg(g=32) == ESHAPE          # below 64
+    assert _gg(N=192, g=128) == ESHAPE  # does not divide N
+    assert _gg(K=5) == ESHAPE
+    assert _gg(K=0) == ESHAPE
+    assert _gg(B=65) == ESHAPE
+    assert _gg(M=0) == OK
+    assert _gg(bits=None) == ENULL
+    assert _gg(alpha=None) == ENULL
+    assert _gg(alpha=A16b + 2) == EALIGN
+    assert _gg(bits=A16 + 4) == EALIGN
+    assert bsg.lib().bsq_pack_grouped_workspace_bytes(64, 256, 128) >= 64 * 256 * 8
+    assert bsg.lib().bsq_pack_grouped_workspace_bytes(64, 256, 96) == 0
+    nb = bsg.lib().bsq_pack_grouped_workspace_bytes(64, 256, 128)
+    pg = bsg.lib().bsq_pack_grouped
+    assert pg(A16, 64, 256, 2, 100, 0, A16b, A16c, None, A16d, nb, None) == ESHAPE
+    assert pg(A16, 64, 256, 2, 128, 1, A16b, A16c, None, A16d, nb, None) == ENULL   # colscale requested
+    assert pg(A16, 64, 256, 2, 128, 0, A16b, A16c, None, A16d, nb - 1, None) == EWS
+    assert pg(A16, 64, 256, 2, 128, 4, A16b, A16c, None, A16d, nb, None) == ESHAPE  # unknown flag
+
+
 @fake_ptrs
 def test_bs_gemv_i8_validation():
     L = bsg.lib()
