@@ -205,13 +205,13 @@ def bsq_pack(W, K: int, colscale: bool = False, workspace=None):
 
 
 def bsq_pack_grouped(W, K: int, g: int, colscale: bool = False, workspace=None):
-    """bsq_pack with one row scale per group of g columns.  Returns (bits, alpha fp32 [K][M][N/g],
-    colscale fp16-bits int16 [K][N] or None)."""
+    """bsq_pack with one row scale per group of g columns.  Returns (bits, alpha fp32 [K][N/g][M]
+    (group-major), colscale fp16-bits int16 [K][N] or None)."""
     torch = _torch()
     M, N = W.shape
     dev = W.device
     bits = torch.empty(layout_words(K, M, N), dtype=torch.int32, device=dev)
-    alpha = torch.empty((K, M, max(1, N // g)), dtype=torch.float32, device=dev)
+    alpha = torch.empty((K, max(1, N // g), M), dtype=torch.float32, device=dev)
     cs = torch.empty((K, N), dtype=torch.int16, device=dev) if colscale else None
     nb = int(lib().bsq_pack_grouped_workspace_bytes(M, N, g))
     ws = workspace if workspace is not None else torch.empty(max(1, nb), dtype=torch.uint8, device=dev)
@@ -222,7 +222,8 @@ def bsq_pack_grouped(W, K: int, g: int, colscale: bool = False, workspace=None):
 
 
 def bs_gemv_grouped(bits, K: int, M: int, N: int, g: int, alpha, x, colscale=None, y=None, accumulate: bool = False):
-    """y (fp32 [M][B]) = or += the product with group-wise row scales alpha fp32 [K][M][N/g]."""
+    """y (fp32 [M][B]) = or += the product with group-wise row scales alpha fp32 [K][N/g][M]
+    (group-major, as bsq_pack_grouped writes them)."""
     torch = _torch()
     B = _xshape(x, N)
     dev = x.device

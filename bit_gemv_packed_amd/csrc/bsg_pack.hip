@@ -23,8 +23,8 @@ __global__ void k_widen(const float* __restrict__ W, double* __restrict__ R, siz
 
 // mode 0: out[m] = fp32(sum_n |R[m,n]| / N)                (row scale)
 // mode 1: outd[m] = sum_n |W[m,n]| * xbar[n]  (W fp32)      (protected-row score)
-// mode 2: out[m * (N / g) + j] = fp32(sum_{n in group j} |R[m,n]| / g)
-//         (group-wise row scales; g a multiple of the 64-column tile)
+// mode 2: out[j * M + m] = fp32(sum_{n in group j} |R[m,n]| / g)
+//         (group-wise row scales, group-major; g a multiple of the 64-column tile)
 template <int MODE>
 __global__ void __launch_bounds__(kT) k_rowsum(const double* __restrict__ R, const float* __restrict__ W,
                                               const float* __restrict__ xbar, int M, int N,
@@ -53,7 +53,7 @@ __global__ void __launch_bounds__(kT) k_rowsum(const double* __restrict__ R, con
     __syncthreads();
     if (MODE == 2 && (n0 + kT) % g == 0) {  // end of group (n0 + kT) / g - 1
       const int m = m0 + t;
-      if (m < M) out[(size_t)m * (N / g) + (n0 + kT) / g - 1] = (float)(acc / (double)g);
+      if (m < M) out[(size_t)((n0 + kT) / g - 1) * M + m] = (float)(acc / (double)g);
       acc = 0.0;
     }
   }
@@ -125,14 +125,14 @@ __global__ void k_residual(double* __restrict__ R, const float* __restrict__ alp
   }
 }
 
-// Group-wise row scales alpha [M][G] (G = N / g): den[j] = sum_m alpha[m][j]^2,
+// Group-wise row scales alpha [G][M] (G = N / g, group-major): den[j] = sum_m alpha[m][j]^2,
 // cs[n] = fp16(fp32(sum_m alpha[m][j] |R[m,n]| / den[j])) for the group j of
 // n (1 when den[j] == 0), and the residual update with alpha[m][j(n)].
 __global__ void k_den_grouped(const float* __restrict__ alpha, int M, int G, double* __restrict__ den) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= G) return;
   double s = 0.0;
-  for (int m = 0; m < M; ++m) s = s + (double)alpha[(size_t)m * G + j] * (double)alpha[(size_t)m * G + j];
+  for (int m = 0; m < M; ++m) s = s + (double)alpha[(size_t)j * M + m] * (double)alpha[(size_t)j * M + m];
   den[j] = s;
 }
 
@@ -140,14 +140,14 @@ __global__ void k_colscale_grouped(const double* __restrict__ R, const float* __
                                    const double* __restrict__ den, int M, int N, int g, uint16_t* __restrict__ cs) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
-  const int G = N / g, j = n / g;
+  const int j = n / g;
   const double d = den[j];
   uint16_t h;
   if (d == 0.0) {
     h = 0x3c00u;
   } else {
     double num = 0.0;
-    for (int m = 0; m < M; ++m) num = num + (double)alpha[(size_t)m * G + j] * fabs(R[(size_t)m * N + n]);
+    for (int m = 0; m < M; ++m) num = num + (double)alpha[(size_t)j * M + m] * fabs(R[(size_t)m * N + n]);
     const float c32 = (float)(num / d);
     const _Float16 c16 = (_Float16)c32;
     __builtin_memcpy(&h, &c16, 2);
@@ -158,14 +158,13 @@ __global__ void k_colscale_grouped(const double* __restrict__ R, const float* __
 __global__ void k_residual_grouped(double* __restrict__ R, const float* __restrict__ alpha,
                                    const uint16_t* __restrict__ cs, int M, int N, int g) {
   const size_t total = (size_t)M * N;
-  const int G = N / g;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const int m = (int)(i / N);
     const int n = (int)(i % N);
     const double r = R[i];
     const double sgn = r >= 0.0 ? 1.0 : -1.0;
     const double c = cs ? (double)f16_bits_to_float(cs[n]) : 1.0;
-    const double t = (double)alpha[(size_t)m * G + n / g] * c;
+    const double t = (double)alpha[(size_t)(n / g) * M + m] * c;
     R[i] = r - t * sgn;
   }
 }

@@ -334,7 +334,7 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB, GS), (KM <= 2 && B
 #pragma unroll
     for (int k = 0; k < KM; ++k)
       if (base_active<KM>(a, k))
-        d[k] = __uint_as_float(ld32(alsrc, (uint32_t)((k * a.M + m) * a.ngrp + j) * 4u));
+        d[k] = __uint_as_float(ld32(alsrc, (uint32_t)((k * a.ngrp + j) * a.M + m) * 4u));
   };
   load_chunk<KM, NWL>(a, srows, c0 * CW + q * NWL, wb0);
   if (GS) load_gscale(0, ab0);

@@ -226,7 +226,9 @@ BSG_API bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const floa
  *            for the group j of column n (BSG_PACK_COLSCALE; 1 when the
  *            denominator is 0)
  *   R <- R - alpha_k[m][j(n)] c_k[n] B_k[m,n]
- *   alpha     (device) out: fp32 [K][M][N/g]
+ *   alpha     (device) out: fp32 [K][N/g][M], group-major (alpha_k[m][j] at
+ *             (k * (N/g) + j) * M + m: the scales of one group are contiguous
+ *             over the rows, so a wavefront's rows read them in one access)
  *   other arguments as bsq_pack; workspace >= bsq_pack_grouped_workspace_bytes.
  * g a power of two >= 64 dividing N (N % 32 == 0).  g = N gives bsq_pack's
  * result.  fp64 sums in ascending order: bit-exact with a sequential
@@ -239,13 +241,13 @@ BSG_API bsg_status bsq_pack_grouped(const float* W, int M, int N, int K, int g, 
 
 /*
  * bs_gemv_grouped -- bs_gemv with group-wise row scales (FluxBin Sec. 3.1):
- *   y[m,b] (= or +=) sum_k sum_j alpha[k][m][j] *
+ *   y[m,b] (= or +=) sum_k sum_j alpha_k[m][j] *
  *                    sum_{n in group j} (2 bit_k(m,n) - 1) * c_k[n] * x[n,b]
- *   alpha     (device) fp32 [K][M][N/g]
+ *   alpha     (device) fp32 [K][N/g][M], group-major as bsq_pack_grouped writes it
  *   other arguments as bs_gemv.
  * 1 <= K <= 4, g a power of two >= 64 dividing N, 1 <= B <= 64 (one launch
  * per batch column).  fp32 sums in a fixed order, within
- * 2e-3 * sum_k sum_j |alpha[k][m][j]| * sum_{n in j} |c_k[n] x[n,b]|.
+ * 2e-3 * sum_k sum_j |alpha_k[m][j]| * sum_{n in j} |c_k[n] x[n,b]|.
  */
 BSG_API bsg_status bs_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, const float* alpha,
                                    const uint16_t* colscale, const void* x, int x_dtype, int B, float* y,

@@ -5,7 +5,8 @@ within the per-output bound
 
     2e-3 * sum_k sum_n |alpha_k[m][n / g]| * |c_k[n]| * |x[n, b]|
 
-(the fp16 column scales c_k are 1 when absent).
+(the fp16 column scales c_k are 1 when absent).  The library keeps the
+scales group-major, [K][N/g][M]; the oracle row-major, [K][M][N/g].
 
 Cases cover group widths 64 (which forces more lanes per row than the
 ungrouped plan), 128 and 256; one to four bases; ragged M; bf16, fp16 and
@@ -23,6 +24,11 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 import bit_gemv_packed_amd as bsg  # noqa: E402
+
+
+def _gm(alpha):
+    """Oracle scales [K][M][N/g] -> the library's group-major [K][N/g][M]."""
+    return np.ascontiguousarray(np.asarray(alpha).transpose(0, 2, 1))
 
 
 def _tol(alpha, cs, x, g, rel=2e-3):
@@ -56,7 +62,7 @@ def test_pack_grouped_bit_exact(case):
     torch.cuda.synchronize()
     rb, ra, rc = oracle.pack_grouped(W, K, g, cs)
     np.testing.assert_array_equal(u32(bsg.bsg_layout_to_logical(bits, K, M, N)).reshape(K, M, -1), rb)
-    np.testing.assert_array_equal(alpha.cpu().numpy().view(np.uint32), ra.view(np.uint32))
+    np.testing.assert_array_equal(alpha.cpu().numpy().view(np.uint32), _gm(ra).view(np.uint32))
     if cs:
         np.testing.assert_array_equal(u16(csd), rc)
 
@@ -95,7 +101,7 @@ def test_gemv_grouped_matches_oracle(case):
     say("bs_gemv_grouped", case)
     L, alpha, csb, x = _inputs(M, N, K, g, B, cs, dt, M * 3 + N + K + g + B)
     bits = bsg.bsg_logical_to_layout(to_dev(L.view(np.int32)), K, M, N)
-    y = bsg.bs_gemv_grouped(bits, K, M, N, g, to_dev(alpha), x_dev(x, dt),
+    y = bsg.bs_gemv_grouped(bits, K, M, N, g, to_dev(_gm(alpha)), x_dev(x, dt),
                             colscale=f16_dev(csb) if cs else None)
     torch.cuda.synchronize()
     ref = oracle.sign_gemv_grouped(L, K, M, N, g, alpha, x, csb)
@@ -109,7 +115,7 @@ def test_gemv_grouped_accumulates():
     bits = bsg.bsg_logical_to_layout(to_dev(L.view(np.int32)), K, M, N)
     y0 = np.random.default_rng(5).standard_normal((M, B)).astype(np.float32)
     y = to_dev(y0)
-    bsg.bs_gemv_grouped(bits, K, M, N, g, to_dev(alpha), x_dev(x, "bf16"), colscale=f16_dev(csb),
+    bsg.bs_gemv_grouped(bits, K, M, N, g, to_dev(_gm(alpha)), x_dev(x, "bf16"), colscale=f16_dev(csb),
                         y=y, accumulate=True)
     torch.cuda.synchronize()
     ref = oracle.sign_gemv_grouped(L, K, M, N, g, alpha, x, csb) + y0
@@ -125,7 +131,7 @@ def test_gemv_grouped_with_one_group_equals_ungrouped():
     L, alpha, csb, x = _inputs(M, N, K, N, 1, True, "bf16", 77)
     bits = bsg.bsg_logical_to_layout(to_dev(L.view(np.int32)), K, M, N)
     a2 = alpha.reshape(K, M)
-    yg = bsg.bs_gemv_grouped(bits, K, M, N, N, to_dev(alpha), x_dev(x, "bf16"), colscale=f16_dev(csb))
+    yg = bsg.bs_gemv_grouped(bits, K, M, N, N, to_dev(_gm(alpha)), x_dev(x, "bf16"), colscale=f16_dev(csb))
     y1 = bsg.bs_gemv(bits, K, M, N, to_dev(a2), x_dev(x, "bf16"), colscale=f16_dev(csb))
     torch.cuda.synchronize()
     ref = oracle.sign_gemv(L, K, M, N, a2, x, csb)
