@@ -67,6 +67,8 @@ def lib():
             "or_binlr_fit": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
             "or_pack_grouped": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P]),
             "or_sign_gemv_grouped": (None, [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P]),
+            "or_pack_hybrid": (_I, [_P, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P]),
+            "or_sign_gemv_hybrid": (None, [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -235,13 +237,13 @@ def salient_select(W, xbar, ns: int, alpha=None):
 
 # ---------------------------------------------------------------- layout
 def pack_grouped(W, K: int, g: int, with_colscale: bool = False):
-    """Greedy residual bases with one row scale per group of g columns (FluxBin Sec. 3.1); see
-    or_pack_grouped.  Returns (bits [K][M][ceil(N/32)], alpha fp32 [K][M][N/g], colscale fp16 bits [K][N]
-    or None)."""
+    """Greedy residual bases with one fp16 row scale per group of g columns (FluxBin Sec. 3.1,
+    App. C.2); see or_pack_grouped.  Returns (bits [K][M][ceil(N/32)], alpha fp16 bits [K][M][N/g],
+    colscale fp16 bits [K][N] or None)."""
     W = _c(np.asarray(W, np.float32), np.float32)
     M, N = W.shape
     bits = np.zeros((K, M, words(N)), np.uint32)
-    alpha = np.zeros((K, M, N // g), np.float32)
+    alpha = np.zeros((K, M, N // g), np.uint16)
     cs = np.zeros((K, N), np.uint16) if with_colscale else None
     rc = lib().or_pack_grouped(_ptr(W), M, N, K, g, 1 if with_colscale else 0, _ptr(bits), _ptr(alpha), _ptr(cs))
     if rc != 0:
@@ -250,19 +252,78 @@ def pack_grouped(W, K: int, g: int, with_colscale: bool = False):
 
 
 def sign_gemv_grouped(bits, K, M, N, g, alpha, x, colscale_f16=None) -> np.ndarray:
-    """y [M][B] in float64 for group-wise row scales alpha fp32 [K][M][N/g]."""
+    """y [M][B] in float64 for group-wise row scales alpha fp16 bits [K][M][N/g]."""
     x = np.asarray(x, np.float64)
     if x.ndim == 1:
         x = x[:, None]
     B = x.shape[1]
     bits = _c(bits, np.uint32).reshape(-1)
-    a = _c(np.asarray(alpha, np.float32), np.float32).reshape(-1)
+    a = _c(np.asarray(alpha, np.uint16), np.uint16).reshape(-1)
     assert a.size == K * M * (N // g)
     cs = None if colscale_f16 is None else _c(np.asarray(colscale_f16, np.uint16), np.uint16).reshape(-1)
     xc = _c(x, np.float64)
     y = np.zeros((M, B), np.float64)
     lib().or_sign_gemv_grouped(_ptr(bits), K, M, N, g, _ptr(a), _ptr(cs), _ptr(xc), B, _ptr(y))
     return y
+
+
+def pack_hybrid(W, K: int, g: int, s: int, idx, with_colscale: bool = False):
+    """Global grouped bases plus salient-column refinement through a dense physical matrix (FluxBin
+    Sec. 3.1 hybrid bases, Sec. 3.2 VCM); see or_pack_hybrid.  idx: int32 [s * N/g] column indices.
+    Returns (bits, alpha, colscale, sbits [K][M][ceil(S/32)], salpha fp16 bits [K][M][N/g],
+    scolscale fp16 bits [K][S] or None)."""
+    W = _c(np.asarray(W, np.float32), np.float32)
+    M, N = W.shape
+    G = N // g
+    S = s * G
+    idx = _c(np.asarray(idx, np.int32), np.int32)
+    assert idx.size == S
+    bits = np.zeros((K, M, words(N)), np.uint32)
+    alpha = np.zeros((K, M, G), np.uint16)
+    cs = np.zeros((K, N), np.uint16) if with_colscale else None
+    sbits = np.zeros((K, M, words(S)), np.uint32)
+    salpha = np.zeros((K, M, G), np.uint16)
+    scs = np.zeros((K, S), np.uint16) if with_colscale else None
+    rc = lib().or_pack_hybrid(_ptr(W), M, N, K, g, s, _ptr(idx), 1 if with_colscale else 0, _ptr(bits),
+                              _ptr(alpha), _ptr(cs), _ptr(sbits), _ptr(salpha), _ptr(scs))
+    if rc != 0:
+        raise ValueError("pack_hybrid failed (%d)" % rc)
+    return bits, alpha, cs, sbits, salpha, scs
+
+
+def sign_gemv_hybrid(bits, K, M, N, g, alpha, colscale_f16, sbits, s, idx, salpha, scolscale_f16, x) -> np.ndarray:
+    """y [M][B] in float64: the grouped product plus the salient branch on x[idx]; see or_sign_gemv_hybrid."""
+    x = np.asarray(x, np.float64)
+    if x.ndim == 1:
+        x = x[:, None]
+    B = x.shape[1]
+    G = N // g
+    S = s * G
+    u16 = lambda a: None if a is None else _c(np.asarray(a, np.uint16), np.uint16).reshape(-1)
+    bits = _c(bits, np.uint32).reshape(-1)
+    sbits = _c(sbits, np.uint32).reshape(-1)
+    idx = _c(np.asarray(idx, np.int32), np.int32).reshape(-1)
+    assert idx.size == S and sbits.size == K * M * words(S)
+    a, cs, sa, scs = u16(alpha), u16(colscale_f16), u16(salpha), u16(scolscale_f16)
+    assert a.size == K * M * G and sa.size == K * M * G
+    xc = _c(x, np.float64)
+    y = np.zeros((M, B), np.float64)
+    lib().or_sign_gemv_hybrid(_ptr(bits), K, M, N, g, _ptr(a), _ptr(cs), _ptr(sbits), s, _ptr(idx), _ptr(sa),
+                              _ptr(scs), _ptr(xc), B, _ptr(y))
+    return y
+
+
+def average_bits(K: int, M: int, N: int, g: int, s: int = 0, colscale: bool = True, scale_bits: int = 16) -> float:
+    """Effective average bit-width of the stored format (FluxBin App. C.2 storage analysis: every
+    scale and index stored in 16 bits): bits of the K global bases, their group row scales and
+    column scales, and for s > 0 the K salient bases over S = s N/g columns, their group row scales,
+    column scales and the S column indices, over the M N weights."""
+    G = N // g
+    S = s * G
+    total = K * M * N + K * M * G * scale_bits + (K * N * scale_bits if colscale else 0)
+    if s:
+        total += K * M * S + K * M * G * scale_bits + (K * S * scale_bits if colscale else 0) + S * 16
+    return total / (M * N)
 
 
 def binlr_fit(W, r: int, vinit, rounds: int = 5):

@@ -443,22 +443,76 @@ OR_API void or_layout_to_logical(const uint32_t* phys, int K, int M, int N, uint
 
 /*
  * Group-wise row scales [FluxBin Sec. 3.1: one row scale per weight group;
- * Sec. 4 setup: group size g = 128 in the Kb-g128 configurations].  The
- * greedy residual recipe of or_pack with the row scale taken per row and
- * per group of g consecutive columns (g divides N; g = N is or_pack):
- *   alpha_k[m][j] = fp32( sum_{n in group j} |R[m,n]| / g )
+ * Sec. 4 setup: group size g = 128 in the Kb-g128 configurations; App. C.2:
+ * every scale is stored in fp16].  The greedy residual recipe of or_pack on
+ * a residual R [M][NC], with the row scale taken per row and per group of g
+ * consecutive columns (g divides NC):
+ *   alpha_k[m][j] = fp16(fp32( sum_{n in group j} |R[m,n]| / g ))
  *   if colscale: c_k[n] = fp16(fp32( num_n / den_j )),
- *                num_n = sum_m alpha_k[m][j] |R[m,n]|, den_j = sum_m
- *                alpha_k[m][j]^2 for the group j of column n (least squares
- *                given the group scales; c = 1 when den_j == 0), else c = 1
- *   R <- R - alpha_k[m][j(n)] * c_k[n] * B_k[m,n]
- * alpha is fp32 [K][M][N/g].  Returns 0, -1 on bad sizes or allocation
- * failure, -2 on a NaN in W.
+ *                num_n = sum_m a_k[m][j] |R[m,n]|, den_j = sum_m a_k[m][j]^2
+ *                with a the stored fp16 group scales, for the group j of
+ *                column n (least squares given the group scales; c = 1 when
+ *                den_j == 0), else c = 1
+ *   R <- R - a_k[m][j(n)] * c_k[n] * B_k[m,n]     (after every base)
+ * bits: logical [K][M][nd] words (nd >= ceil(NC/32); bits past NC clear);
+ * alpha: fp16 bits [K][M][NC/g]; colscale fp16 bits [K][NC] or NULL.
+ * cdbl: NC doubles of scratch.
+ */
+static void grouped_bases(double* R, int M, int NC, int nd, int K, int g, uint32_t* bits, uint16_t* alpha,
+                          uint16_t* colscale, double* cdbl) {
+  const int G = NC / g;
+  for (int k = 0; k < K; ++k) {
+    uint32_t* bk = bits + (size_t)k * M * nd;
+    uint16_t* ak = alpha + (size_t)k * M * G;   /* ak[m * G + j] */
+    for (int m = 0; m < M; ++m)
+      for (int n = 0; n < NC; ++n)
+        if (R[(size_t)m * NC + n] >= 0.0) bk[(size_t)m * nd + (n >> 5)] |= 1u << (n & 31);
+    for (int m = 0; m < M; ++m)
+      for (int j = 0; j < G; ++j) {
+        double s = 0.0;
+        for (int n = j * g; n < (j + 1) * g; ++n) s += fabs(R[(size_t)m * NC + n]);
+        ak[(size_t)m * G + j] = or_f32_to_f16((float)(s / (double)g));
+      }
+    for (int n = 0; n < NC; ++n) cdbl[n] = 1.0;
+    if (colscale) {
+      for (int j = 0; j < G; ++j) {
+        double den = 0.0;
+        for (int m = 0; m < M; ++m) {
+          const double a = or_f16_to_f64(ak[(size_t)m * G + j]);
+          den += a * a;
+        }
+        for (int n = j * g; n < (j + 1) * g; ++n) {
+          uint16_t h;
+          if (den == 0.0) {
+            h = 0x3c00u;
+          } else {
+            double num = 0.0;
+            for (int m = 0; m < M; ++m) num += or_f16_to_f64(ak[(size_t)m * G + j]) * fabs(R[(size_t)m * NC + n]);
+            h = or_f32_to_f16((float)(num / den));
+          }
+          colscale[(size_t)k * NC + n] = h;
+          cdbl[n] = or_f16_to_f64(h);
+        }
+      }
+    }
+    for (int m = 0; m < M; ++m)
+      for (int n = 0; n < NC; ++n) {
+        double sgn = (bk[(size_t)m * nd + (n >> 5)] >> (n & 31)) & 1u ? 1.0 : -1.0;
+        double t = or_f16_to_f64(ak[(size_t)m * G + n / g]) * cdbl[n];
+        R[(size_t)m * NC + n] = R[(size_t)m * NC + n] - t * sgn;
+      }
+  }
+}
+
+/*
+ * or_pack_grouped: grouped_bases on R = W [M][N].  alpha is fp16 bits
+ * [K][M][N/g].  Returns 0, -1 on bad sizes or allocation failure, -2 on a
+ * NaN in W.
  */
 OR_API int or_pack_grouped(const float* W, int M, int N, int K, int g, int with_colscale,
-                           uint32_t* bits, float* alpha, uint16_t* colscale) {
+                           uint32_t* bits, uint16_t* alpha, uint16_t* colscale) {
   if (g <= 0 || N % g != 0) return -1;
-  const int nd = (N + 31) / 32, G = N / g;
+  const int nd = (N + 31) / 32;
   const size_t mn = (size_t)M * N;
   double* R = (double*)malloc(sizeof(double) * (mn ? mn : 1));
   double* cdbl = (double*)malloc(sizeof(double) * (N > 0 ? N : 1));
@@ -468,45 +522,54 @@ OR_API int or_pack_grouped(const float* W, int M, int N, int K, int g, int with_
     R[i] = (double)W[i];
   }
   memset(bits, 0, sizeof(uint32_t) * (size_t)K * M * nd);
-  for (int k = 0; k < K; ++k) {
-    uint32_t* bk = bits + (size_t)k * M * nd;
-    float* ak = alpha + (size_t)k * M * G;   /* ak[m * G + j] */
-    for (int m = 0; m < M; ++m)
-      for (int n = 0; n < N; ++n)
-        if (R[(size_t)m * N + n] >= 0.0) bk[(size_t)m * nd + (n >> 5)] |= 1u << (n & 31);
-    for (int m = 0; m < M; ++m)
-      for (int j = 0; j < G; ++j) {
-        double s = 0.0;
-        for (int n = j * g; n < (j + 1) * g; ++n) s += fabs(R[(size_t)m * N + n]);
-        ak[(size_t)m * G + j] = (float)(s / (double)g);
-      }
-    for (int n = 0; n < N; ++n) cdbl[n] = 1.0;
-    if (with_colscale) {
-      for (int j = 0; j < G; ++j) {
-        double den = 0.0;
-        for (int m = 0; m < M; ++m) den += (double)ak[(size_t)m * G + j] * (double)ak[(size_t)m * G + j];
-        for (int n = j * g; n < (j + 1) * g; ++n) {
-          uint16_t h;
-          if (den == 0.0) {
-            h = 0x3c00u;
-          } else {
-            double num = 0.0;
-            for (int m = 0; m < M; ++m) num += (double)ak[(size_t)m * G + j] * fabs(R[(size_t)m * N + n]);
-            h = or_f32_to_f16((float)(num / den));
-          }
-          colscale[(size_t)k * N + n] = h;
-          cdbl[n] = or_f16_to_f64(h);
-        }
-      }
-    }
-    for (int m = 0; m < M; ++m)
-      for (int n = 0; n < N; ++n) {
-        double sgn = (bk[(size_t)m * nd + (n >> 5)] >> (n & 31)) & 1u ? 1.0 : -1.0;
-        double t = (double)ak[(size_t)m * G + n / g] * cdbl[n];
-        R[(size_t)m * N + n] = R[(size_t)m * N + n] - t * sgn;
-      }
-  }
+  grouped_bases(R, M, N, nd, K, g, bits, alpha, with_colscale ? colscale : NULL, cdbl);
   free(cdbl);
+  free(R);
+  return 0;
+}
+
+/*
+ * Hybrid bases with salient-column refinement [FluxBin Sec. 3.1 "Structural
+ * Saliency Search" (extra bases on the salient columns), Sec. 3.2 "Virtual
+ * Columnar Mapping" (the sparse salient columns are stored as a dense
+ * physical matrix; an index list gathers x and the scales), Sec. 4 setup
+ * (Kb-sS-gG: the same base count K for both branches, s salient columns per
+ * group of g)].  Reading (the pages give no equation for the refinement):
+ *   1. the global branch: grouped_bases on R = W with K bases and groups of g;
+ *   2. the salient branch: the residual left by step 1 at the S = s * (N/g)
+ *      columns idx[0..S) (idx[j*s .. j*s+s) normally the salient columns of
+ *      group j, chosen by the caller: the saliency search needs calibration
+ *      Hessians) gathered into the dense matrix Rs[m][p] = R[m][idx[p]], and
+ *      grouped_bases on Rs with K bases and groups of s physical columns.
+ * sbits: logical [K][M][ceil(S/32)] (bits past S clear); salpha fp16 bits
+ * [K][M][S/s]; scolscale fp16 bits [K][S] or NULL (with colscale).
+ * Returns 0, -1 on bad sizes, an index outside [0, N) or allocation failure,
+ * -2 on a NaN in W.
+ */
+OR_API int or_pack_hybrid(const float* W, int M, int N, int K, int g, int s, const int32_t* idx, int with_colscale,
+                          uint32_t* bits, uint16_t* alpha, uint16_t* colscale, uint32_t* sbits, uint16_t* salpha,
+                          uint16_t* scolscale) {
+  if (g <= 0 || N % g != 0 || s <= 0 || s > g) return -1;
+  const int nd = (N + 31) / 32, S = s * (N / g), nds = (S + 31) / 32;
+  for (int p = 0; p < S; ++p)
+    if (idx[p] < 0 || idx[p] >= N) return -1;
+  const size_t mn = (size_t)M * N;
+  double* R = (double*)malloc(sizeof(double) * (mn ? mn : 1));
+  double* Rs = (double*)malloc(sizeof(double) * ((size_t)M * S > 0 ? (size_t)M * S : 1));
+  double* cdbl = (double*)malloc(sizeof(double) * (N > 0 ? N : 1));
+  if (!R || !Rs || !cdbl) { free(R); free(Rs); free(cdbl); return -1; }
+  for (size_t i = 0; i < mn; ++i) {
+    if (isnan(W[i])) { free(R); free(Rs); free(cdbl); return -2; }
+    R[i] = (double)W[i];
+  }
+  memset(bits, 0, sizeof(uint32_t) * (size_t)K * M * nd);
+  memset(sbits, 0, sizeof(uint32_t) * (size_t)K * M * nds);
+  grouped_bases(R, M, N, nd, K, g, bits, alpha, with_colscale ? colscale : NULL, cdbl);
+  for (int m = 0; m < M; ++m)
+    for (int p = 0; p < S; ++p) Rs[(size_t)m * S + p] = R[(size_t)m * N + idx[p]];
+  grouped_bases(Rs, M, S, nds, K, s, sbits, salpha, with_colscale ? scolscale : NULL, cdbl);
+  free(cdbl);
+  free(Rs);
   free(R);
   return 0;
 }
@@ -514,10 +577,10 @@ OR_API int or_pack_grouped(const float* W, int M, int N, int K, int g, int with_
 /*
  * The product with group-wise row scales [FluxBin Sec. 3.1]:
  *   y[m,b] = sum_k sum_j alpha_k[m][j] sum_{n in group j} (2 bit_k(m,n) - 1) c_k[n] x[n,b]
- * alpha fp32 [K][M][N/g]; colscale fp16 bits [K][N] or NULL; x [N][B]
+ * alpha fp16 bits [K][M][N/g]; colscale fp16 bits [K][N] or NULL; x [N][B]
  * (double); y [M][B] double.  Sums in double, ascending order.
  */
-OR_API void or_sign_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, const float* alpha,
+OR_API void or_sign_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, const uint16_t* alpha,
                                  const uint16_t* colscale, const double* x, int B, double* y) {
   const int nd = (N + 31) / 32, G = N / g;
   for (int m = 0; m < M; ++m)
@@ -531,9 +594,39 @@ OR_API void or_sign_gemv_grouped(const uint32_t* bits, int K, int M, int N, int 
             const double c = colscale ? or_f16_to_f64(colscale[(size_t)k * N + n]) : 1.0;
             acc += (bit ? 1.0 : -1.0) * c * x[(size_t)n * B + b];
           }
-          tot += (double)alpha[((size_t)k * M + m) * G + j] * acc;
+          tot += or_f16_to_f64(alpha[((size_t)k * M + m) * G + j]) * acc;
         }
       y[(size_t)m * B + b] = tot;
+    }
+}
+
+/*
+ * The hybrid product [FluxBin Sec. 3.2 VCM]: the global grouped product plus
+ * the salient branch on the gathered activations,
+ *   y[m,b] += sum_k sum_j salpha_k[m][j] sum_{i < s} (2 sbit_k(m, j*s+i) - 1)
+ *                                        sc_k[j*s+i] x[idx[j*s+i], b]
+ * (S = s * (N/g) physical salient columns; sbits logical [K][M][ceil(S/32)]).
+ */
+OR_API void or_sign_gemv_hybrid(const uint32_t* bits, int K, int M, int N, int g, const uint16_t* alpha,
+                                const uint16_t* colscale, const uint32_t* sbits, int s, const int32_t* idx,
+                                const uint16_t* salpha, const uint16_t* scolscale, const double* x, int B,
+                                double* y) {
+  or_sign_gemv_grouped(bits, K, M, N, g, alpha, colscale, x, B, y);
+  const int G = N / g, S = s * G, nds = (S + 31) / 32;
+  for (int m = 0; m < M; ++m)
+    for (int b = 0; b < B; ++b) {
+      double tot = 0.0;
+      for (int k = 0; k < K; ++k)
+        for (int j = 0; j < G; ++j) {
+          double acc = 0.0;
+          for (int p = j * s; p < (j + 1) * s; ++p) {
+            const int bit = (sbits[((size_t)k * M + m) * nds + (p >> 5)] >> (p & 31)) & 1u;
+            const double c = scolscale ? or_f16_to_f64(scolscale[(size_t)k * S + p]) : 1.0;
+            acc += (bit ? 1.0 : -1.0) * c * x[(size_t)idx[p] * B + b];
+          }
+          tot += or_f16_to_f64(salpha[((size_t)k * M + m) * G + j]) * acc;
+        }
+      y[(size_t)m * B + b] += tot;
     }
 }
 

@@ -572,20 +572,20 @@ def test_lr_fit_singular_refit_keeps_the_greedy_coefficients():
 
 
 # ----------------------------------------------------------- group-wise row scales
-@pytest.mark.parametrize("cs", [False, True])
-def test_grouped_pack_with_one_group_is_the_row_scale_pack(cs):
-    """g = N: one group per row, the recipe of or_pack (bits, scales bit for bit)."""
-    M, N, K = 12, 96, 2
+def test_grouped_pack_with_one_group_is_the_row_scale_pack():
+    """g = N: one group per row.  The first base is or_pack's (the same signs;
+    the scale is or_pack's fp32 mean rounded to fp16), and the product with
+    those scales is or_sign_gemv's with the same values."""
+    M, N = 12, 96
     W = synth.weights(61, 0, M, N)
-    b1, a1, c1 = oracle.pack(W, K, cs)
-    b2, a2, c2 = oracle.pack_grouped(W, K, N, cs)
+    b1, a1, _ = oracle.pack(W, 1, False)
+    b2, a2, _ = oracle.pack_grouped(W, 1, N, False)
     np.testing.assert_array_equal(b1, b2)
-    np.testing.assert_array_equal(a1.view(np.uint32), a2[:, :, 0].view(np.uint32))
-    if cs:
-        np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(a2[:, :, 0], oracle.f32_to_f16(a1))
     x = synth.random_x(61, N, 2, "f32")
-    np.testing.assert_array_equal(oracle.sign_gemv(b1, K, M, N, a1, x, c1),
-                                  oracle.sign_gemv_grouped(b2, K, M, N, N, a2, x, c2))
+    a16 = oracle.f16_to_f64(a2[:, :, 0]).astype(np.float32)
+    np.testing.assert_array_equal(oracle.sign_gemv(b1, 1, M, N, a16, x),
+                                  oracle.sign_gemv_grouped(b2, 1, M, N, N, a2, x))
 
 
 @pytest.mark.parametrize("cs", [False, True])
@@ -595,20 +595,22 @@ def test_grouped_product_equals_the_dense_dequantised_matmul(cs):
     bits, alpha, csb = oracle.pack_grouped(W, K, g, cs)
     S = _dense_signs(bits, K, M, N)
     c = oracle.f16_to_f64(csb).reshape(K, N) if cs else np.ones((K, N))
-    a = np.repeat(alpha.astype(np.float64), g, axis=2)          # [K][M][N]: the scale of each entry's group
+    a = np.repeat(oracle.f16_to_f64(alpha), g, axis=2)          # [K][M][N]: the scale of each entry's group
     What = (a * c[:, None, :] * S).sum(0)
     x = synth.random_x(62, N, 3, "f32").astype(np.float64)
     np.testing.assert_allclose(oracle.sign_gemv_grouped(bits, K, M, N, g, alpha, x, csb), What @ x,
                                rtol=1e-12, atol=1e-15)
 
 
-def test_grouped_alpha_is_the_fp32_argmin_per_group():
-    """Moving a group scale by one fp32 ulp either way never lowers that
-    group's error (exact rationals)."""
+def test_grouped_alpha_is_the_fp16_argmin_per_group():
+    """Moving a group scale by one fp16 step either way never lowers that
+    group's error (exact rationals): the stored fp16 scale is the best fp16
+    value for its group."""
     M, N, g = 4, 96, 32
     W = synth.weights(63, 0, M, N)
     bits, alpha, _ = oracle.pack_grouped(W, 1, g, False)
     S = _dense_signs(bits, 1, M, N)[0]
+    a16 = alpha.view(np.float16)
     for m in range(M):
         for j in range(N // g):
             R = [Fraction(float(v)) for v in W[m, j * g:(j + 1) * g]]
@@ -618,29 +620,31 @@ def test_grouped_alpha_is_the_fp32_argmin_per_group():
                 a = Fraction(float(a))
                 return sum((r - a * si) ** 2 for r, si in zip(R, sg))
 
-            a0 = alpha[0, m, j]
+            a0 = a16[0, m, j]
             base = sse(a0)
             for d in (np.inf, -np.inf):
-                assert sse(np.nextafter(a0, np.float32(d))) >= base
+                assert sse(np.nextafter(a0, np.float16(d))) >= base
 
 
 def test_grouped_colscale_is_the_least_squares_value_per_group():
-    """c[n] = fp16(fp32(sum_m alpha[m][j] |R| / sum_m alpha[m][j]^2)) with the
-    group j of column n, written out in exact rationals for the first base."""
+    """c[n] = fp16(fp32(sum_m a[m][j] |R| / sum_m a[m][j]^2)) with the stored
+    fp16 scales a of the group j of column n, in exact rationals (first base)."""
     M, N, g = 5, 64, 32
     W = synth.weights(64, 0, M, N)
     bits, alpha, cs = oracle.pack_grouped(W, 1, g, True)
+    a = oracle.f16_to_f64(alpha)
     for n in range(N):
         j = n // g
-        num = sum(Fraction(float(alpha[0, m, j])) * abs(Fraction(float(W[m, n]))) for m in range(M))
-        den = sum(Fraction(float(alpha[0, m, j])) ** 2 for m in range(M))
+        num = sum(Fraction(float(a[0, m, j])) * abs(Fraction(float(W[m, n]))) for m in range(M))
+        den = sum(Fraction(float(a[0, m, j])) ** 2 for m in range(M))
         want = oracle.f32_to_f16(np.array([np.float32(float(num / den))], np.float32))[0]
         assert cs[0, n] == want
 
 
 def test_grouped_scales_never_fit_worse_than_row_scales():
     """Same signs, scales fitted per group instead of per row: the error of
-    the first base cannot grow (each group scale is optimal on its group)."""
+    the first base does not grow (each group scale is optimal on its group;
+    fp16 storage costs far less than the grouping gains here)."""
     M, N = 16, 512
     W = synth.weights(65, 0, M, N)
     Wd = W.astype(np.float64)
@@ -649,5 +653,90 @@ def test_grouped_scales_never_fit_worse_than_row_scales():
     np.testing.assert_array_equal(b1, b2)
     S = _dense_signs(b1, 1, M, N)[0]
     e_row = ((Wd - a1[0].astype(np.float64)[:, None] * S) ** 2).sum()
-    e_grp = ((Wd - np.repeat(a2[0].astype(np.float64), 128, axis=1) * S) ** 2).sum()
-    assert e_grp <= e_row * (1 + 1e-7)
+    e_grp = ((Wd - np.repeat(oracle.f16_to_f64(a2[0]), 128, axis=1) * S) ** 2).sum()
+    assert e_grp <= e_row
+
+
+# ----------------------------------------------------------- salient columns (VCM)
+def _group_idx(seed, N, g, s):
+    """s distinct ascending columns of every group of g (seeded)."""
+    r = np.random.default_rng(seed)
+    return np.concatenate([np.sort(r.choice(g, s, replace=False)) + j * g for j in range(N // g)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("cs", [False, True])
+def test_hybrid_with_every_column_salient_continues_the_greedy_bases(cs):
+    """s = g and idx = 0..N-1: the salient branch sees the global residual in
+    place, so its K bases are bases K..2K-1 of the 2K-base grouped pack, bit
+    for bit (signs, fp16 group scales, column scales)."""
+    M, N, K, g = 10, 256, 2, 64
+    W = synth.weights(66, 0, M, N)
+    b, a, c, sb, sa, sc = oracle.pack_hybrid(W, K, g, g, np.arange(N, dtype=np.int32), cs)
+    b2, a2, c2 = oracle.pack_grouped(W, 2 * K, g, cs)
+    np.testing.assert_array_equal(b, b2[:K])
+    np.testing.assert_array_equal(a, a2[:K])
+    np.testing.assert_array_equal(sb, b2[K:])
+    np.testing.assert_array_equal(sa, a2[K:])
+    if cs:
+        np.testing.assert_array_equal(c, c2[:K])
+        np.testing.assert_array_equal(sc, c2[K:])
+
+
+@pytest.mark.parametrize("cs", [False, True])
+def test_hybrid_product_equals_the_dense_dequantised_matmul(cs):
+    """The salient bases scattered back to their logical columns (VCM undone)
+    and added to the global reconstruction give the dense matrix whose
+    product the hybrid product is."""
+    M, N, K, g, s = 7, 256, 2, 64, 8
+    W = synth.weights(67, 0, M, N)
+    idx = _group_idx(67, N, g, s)
+    S = s * (N // g)
+    b, a, c, sb, sa, sc = oracle.pack_hybrid(W, K, g, s, idx, cs)
+    Sg = _dense_signs(b, K, M, N)
+    cg = oracle.f16_to_f64(c) if cs else np.ones((K, N))
+    What = (np.repeat(oracle.f16_to_f64(a), g, axis=2) * cg[:, None, :] * Sg).sum(0)
+    Ss = _dense_signs(sb, K, M, S)
+    csal = oracle.f16_to_f64(sc) if cs else np.ones((K, S))
+    phys = (np.repeat(oracle.f16_to_f64(sa), s, axis=2) * csal[:, None, :] * Ss).sum(0)   # [M][S]
+    for p in range(S):
+        What[:, idx[p]] += phys[:, p]
+    x = synth.random_x(67, N, 2, "f32").astype(np.float64)
+    y = oracle.sign_gemv_hybrid(b, K, M, N, g, a, c, sb, s, idx, sa, sc, x)
+    np.testing.assert_allclose(y, What @ x, rtol=1e-12, atol=1e-14)
+
+
+def test_hybrid_refinement_lowers_the_error_on_the_salient_columns():
+    M, N, K, g, s = 32, 512, 2, 128, 16
+    W = synth.weights(68, 0, M, N)
+    idx = _group_idx(68, N, g, s)
+    b, a, c, sb, sa, sc = oracle.pack_hybrid(W, K, g, s, idx, True)
+    eye = np.eye(N)
+    Wg = oracle.sign_gemv_grouped(b, K, M, N, g, a, eye, c)
+    Wh = oracle.sign_gemv_hybrid(b, K, M, N, g, a, c, sb, s, idx, sa, sc, eye)
+    e_g = ((W[:, idx] - Wg[:, idx]) ** 2).sum()
+    e_h = ((W[:, idx] - Wh[:, idx]) ** 2).sum()
+    assert e_h < 0.5 * e_g
+    rest = np.setdiff1d(np.arange(N), idx)
+    np.testing.assert_array_equal(Wg[:, rest], Wh[:, rest])
+
+
+def test_hybrid_rejects_an_index_outside_the_matrix():
+    W = synth.weights(69, 0, 4, 128)
+    idx = _group_idx(69, 128, 64, 8)
+    idx[3] = 128
+    with pytest.raises(ValueError):
+        oracle.pack_hybrid(W, 1, 64, 8, idx)
+
+
+def test_average_bits_of_the_hybrid_format():
+    """FluxBin App. C.2: with K = 2 global and 2 salient bases, g = 128 and
+    16-bit scales and indices, s = 8 salient columns per group settle at about
+    2.63 bits per weight and s = 16 at about 2.75; without salient columns the
+    two bases and their group scales take 2 + 2*16/128 = 2.25."""
+    assert abs(oracle.average_bits(2, 4096, 4096, 128, 8) - 2.63) < 0.01
+    assert abs(oracle.average_bits(2, 4096, 4096, 128, 16) - 2.75) < 0.015
+    # the per-weight terms alone: K + 16K/g + K s/g + 16K/g
+    big = 1 << 24
+    assert abs(oracle.average_bits(2, big, 4096, 128, 8, colscale=False) - 2.625) < 1e-4
+    assert abs(oracle.average_bits(2, big, 4096, 128, 16, colscale=False) - 2.75) < 1e-4
+    assert abs(oracle.average_bits(2, big, 4096, 128, 0, colscale=False) - 2.25) < 1e-9
