@@ -59,6 +59,9 @@ _SIGS = {
     "bsq_pack_grouped_workspace_bytes": (_SZ, [_I, _I, _I]),
     "bsq_pack_grouped": (ctypes.c_int32, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "bs_gemv_grouped": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P]),
+    "bsq_pack_hybrid_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "bsq_pack_hybrid": (ctypes.c_int32, [_P, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "bs_gemv_hybrid": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P]),
     "binlr_fit_workspace_bytes": (_SZ, [_I, _I, _I]),
     "binlr_fit": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "binlr_apply": (ctypes.c_int32, [_P, _P, _P, _I, _I, _I, _P, _I, _I, _P, _P, _SZ, _P]),
@@ -204,25 +207,65 @@ def bsq_pack(W, K: int, colscale: bool = False, workspace=None):
     return bits, alpha, cs
 
 
-def bsq_pack_grouped(W, K: int, g: int, colscale: bool = False, workspace=None):
-    """bsq_pack with one row scale per group of g columns.  Returns (bits, alpha fp32 [K][N/g][M]
-    (group-major), colscale fp16-bits int16 [K][N] or None)."""
+def salient_cols(N: int, g: int, s: int) -> int:
+    """Physical salient columns S = s * N / g of the hybrid format."""
+    return s * (N // g) if s else 0
+
+
+def salient_scale_shape(K: int, M: int, N: int, g: int, s: int):
+    """Shape of the word-grouped salient row scales: [K][ceil(S/32)][M][32/s]."""
+    return (K, (salient_cols(N, g, s) + 31) // 32, M, 32 // s)
+
+
+def bsq_pack_hybrid(W, K: int, g: int, s: int = 0, idx=None, colscale: bool = False, workspace=None):
+    """Grouped bases (fp16 row scales per group of g, group-major [K][N/g][M]) plus, for s > 0, K
+    salient-column bases over the S = s N/g columns idx (int32 device tensor).  Returns (bits, alpha,
+    colscale or None, sbits or None, salpha or None, scolscale or None); fp16 values as int16."""
     torch = _torch()
     M, N = W.shape
     dev = W.device
+    G = max(1, N // g)
+    S = salient_cols(N, g, s)
     bits = torch.empty(layout_words(K, M, N), dtype=torch.int32, device=dev)
-    alpha = torch.empty((K, max(1, N // g), M), dtype=torch.float32, device=dev)
+    alpha = torch.empty((K, G, M), dtype=torch.int16, device=dev)
     cs = torch.empty((K, N), dtype=torch.int16, device=dev) if colscale else None
-    nb = int(lib().bsq_pack_grouped_workspace_bytes(M, N, g))
+    sbits = salpha = scs = None
+    if s:
+        sp = (S + 31) // 32 * 32
+        sbits = torch.empty(layout_words(K, M, sp), dtype=torch.int32, device=dev)
+        salpha = torch.empty(salient_scale_shape(K, M, N, g, s), dtype=torch.int16, device=dev)
+        scs = torch.empty((K, S), dtype=torch.int16, device=dev) if colscale else None
+    nb = int(lib().bsq_pack_hybrid_workspace_bytes(M, N, g, s))
     ws = workspace if workspace is not None else torch.empty(max(1, nb), dtype=torch.uint8, device=dev)
-    _check("bsq_pack_grouped", lib().bsq_pack_grouped(_ptr(W), M, N, K, g, BSG_PACK_COLSCALE if colscale else 0,
-                                                      _ptr(bits), _ptr(alpha), _ptr(cs), ws.data_ptr(), ws.numel(),
-                                                      _stream(dev)))
-    return bits, alpha, cs
+    _check("bsq_pack_hybrid", lib().bsq_pack_hybrid(
+        _ptr(W), M, N, K, g, s, _ptr(idx), BSG_PACK_COLSCALE if colscale else 0, _ptr(bits), _ptr(alpha), _ptr(cs),
+        _ptr(sbits), _ptr(salpha), _ptr(scs), ws.data_ptr(), ws.numel(), _stream(dev)))
+    return bits, alpha, cs, sbits, salpha, scs
+
+
+def bsq_pack_grouped(W, K: int, g: int, colscale: bool = False, workspace=None):
+    """bsq_pack with one fp16 row scale per group of g columns.  Returns (bits, alpha fp16 bits int16
+    [K][N/g][M] (group-major), colscale fp16 bits int16 [K][N] or None)."""
+    return bsq_pack_hybrid(W, K, g, 0, None, colscale, workspace)[:3]
+
+
+def bs_gemv_hybrid(bits, K: int, M: int, N: int, g: int, alpha, x, colscale=None, sbits=None, s: int = 0,
+                   idx=None, salpha=None, scolscale=None, y=None, accumulate: bool = False):
+    """y (fp32 [M][B]) = or += the grouped product plus, for s > 0, the salient-column bases read
+    through idx (one launch per batch column)."""
+    torch = _torch()
+    B = _xshape(x, N)
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, B), dtype=torch.float32, device=dev)
+    _check("bs_gemv_hybrid", lib().bs_gemv_hybrid(
+        _ptr(bits), K, M, N, g, _ptr(alpha), _ptr(colscale), _ptr(sbits), s, _ptr(idx), _ptr(salpha),
+        _ptr(scolscale), _ptr(x), _dtype_code(x), B, _ptr(y), 1 if accumulate else 0, _stream(dev)))
+    return y
 
 
 def bs_gemv_grouped(bits, K: int, M: int, N: int, g: int, alpha, x, colscale=None, y=None, accumulate: bool = False):
-    """y (fp32 [M][B]) = or += the product with group-wise row scales alpha fp32 [K][N/g][M]
+    """y (fp32 [M][B]) = or += the product with group-wise fp16 row scales alpha [K][N/g][M]
     (group-major, as bsq_pack_grouped writes them)."""
     torch = _torch()
     B = _xshape(x, N)

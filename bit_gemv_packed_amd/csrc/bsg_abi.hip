@@ -10,8 +10,9 @@ namespace bsg {
 hipError_t launch_pack(const float* W, int M, int N, int K, bool colscale, uint32_t* bits, float* alpha,
                        uint16_t* cs, void* ws, hipStream_t st);
 hipError_t launch_pack_signs(const float* S, int M, int N, uint32_t* bits, hipStream_t st);
-hipError_t launch_pack_grouped(const float* W, int M, int N, int K, int g, bool colscale, uint32_t* bits,
-                               float* alpha, uint16_t* cs, void* ws, hipStream_t st);
+hipError_t launch_pack_hybrid(const float* W, int M, int N, int K, int g, int s, const int32_t* idx, bool colscale,
+                              uint32_t* bits, uint16_t* alpha, uint16_t* cs, uint32_t* sbits, uint16_t* salpha,
+                              uint16_t* scs, void* ws, hipStream_t st);
 hipError_t launch_absmean(const float* X, int S, int N, float* xbar, hipStream_t st);
 hipError_t launch_salient(const float* W, int M, int N, const float* xbar, int ns, int32_t* rows, int8_t* q,
                           uint16_t* s, float* alpha, int K, void* ws, hipStream_t st);
@@ -270,42 +271,64 @@ bsg_status bs_gemv_multi(const bsg_proj* projs, int P, int K, int N, const void*
 
 // group size: a power of two >= 64 dividing N
 static bool bad_group(int N, int g) { return g < 64 || (g & (g - 1)) != 0 || N % g != 0; }
+// salient columns per group: 8, 16 or 32 (whole groups per sign word)
+static bool bad_salient(int s) { return s != 8 && s != 16 && s != 32; }
+static int salient_cols(int N, int g, int s) { return s * (N / g); }
+static int salient_words(int N, int g, int s) { return (salient_cols(N, g, s) + 31) / 32; }
 
-size_t bsq_pack_grouped_workspace_bytes(int M, int N, int g) {
-  if (M < 0 || bad_n(N) || bad_group(N, g)) return 0;
-  return align_up((size_t)M * N * 8, 256) + align_up((size_t)(N / g) * 8, 256);
+size_t bsq_pack_hybrid_workspace_bytes(int M, int N, int g, int s) {
+  if (M < 0 || bad_n(N) || bad_group(N, g) || (s != 0 && bad_salient(s))) return 0;
+  return align_up((size_t)M * N * 8, 256) + align_up((size_t)M * salient_cols(N, g, s) * 8, 256) +
+         align_up((size_t)(N / g) * 8, 256);
 }
 
-bsg_status bsq_pack_grouped(const float* W, int M, int N, int K, int g, int flags, uint32_t* bits, float* alpha,
-                            uint16_t* colscale, void* workspace, size_t workspace_bytes, void* stream) {
+size_t bsq_pack_grouped_workspace_bytes(int M, int N, int g) { return bsq_pack_hybrid_workspace_bytes(M, N, g, 0); }
+
+bsg_status bsq_pack_hybrid(const float* W, int M, int N, int K, int g, int s, const int32_t* idx, int flags,
+                           uint32_t* bits, uint16_t* alpha, uint16_t* colscale, uint32_t* sbits, uint16_t* salpha,
+                           uint16_t* scolscale, void* workspace, size_t workspace_bytes, void* stream) {
   const bool cs = (flags & BSG_PACK_COLSCALE) != 0;
-  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || bad_group(N, g) || (flags & ~BSG_PACK_COLSCALE))
+  if (K < 1 || K > kMaxK || M < 0 || bad_n(N) || bad_group(N, g) || (s != 0 && bad_salient(s)) ||
+      (flags & ~BSG_PACK_COLSCALE))
     return BSG_ERR_SHAPE;
   if (M == 0) return BSG_OK;
   if (!W || !bits || !alpha || (cs && !colscale)) return BSG_ERR_NULL;
-  if (misaligned(W, 4) || misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(colscale, 2) ||
+  if (s && (!idx || !sbits || !salpha || (cs && !scolscale))) return BSG_ERR_NULL;
+  if (misaligned(W, 4) || misaligned(bits, 16) || misaligned(alpha, 2) || misaligned(colscale, 2) ||
+      misaligned(idx, 16) || misaligned(sbits, 16) || misaligned(salpha, 8) || misaligned(scolscale, 2) ||
       misaligned(workspace, 16))
     return BSG_ERR_ALIGN;
-  if (!workspace || workspace_bytes < bsq_pack_grouped_workspace_bytes(M, N, g)) return BSG_ERR_WORKSPACE;
-  return hip_status(launch_pack_grouped(W, M, N, K, g, cs, bits, alpha, cs ? colscale : nullptr, workspace,
-                                        (hipStream_t)stream));
+  if (!workspace || workspace_bytes < bsq_pack_hybrid_workspace_bytes(M, N, g, s)) return BSG_ERR_WORKSPACE;
+  return hip_status(launch_pack_hybrid(W, M, N, K, g, s, idx, cs, bits, alpha, cs ? colscale : nullptr, sbits,
+                                       salpha, cs ? scolscale : nullptr, workspace, (hipStream_t)stream));
 }
 
-bsg_status bs_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, const float* alpha,
-                           const uint16_t* colscale, const void* x, int x_dtype, int B, float* y, int accumulate,
-                           void* stream) {
+bsg_status bsq_pack_grouped(const float* W, int M, int N, int K, int g, int flags, uint32_t* bits, uint16_t* alpha,
+                            uint16_t* colscale, void* workspace, size_t workspace_bytes, void* stream) {
+  return bsq_pack_hybrid(W, M, N, K, g, 0, nullptr, flags, bits, alpha, colscale, nullptr, nullptr, nullptr,
+                         workspace, workspace_bytes, stream);
+}
+
+bsg_status bs_gemv_hybrid(const uint32_t* bits, int K, int M, int N, int g, const uint16_t* alpha,
+                          const uint16_t* colscale, const uint32_t* sbits, int s, const int32_t* idx,
+                          const uint16_t* salpha, const uint16_t* scolscale, const void* x, int x_dtype, int B,
+                          float* y, int accumulate, void* stream) {
   if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
-  if (K < 1 || K > 4 || M < 0 || bad_n(N) || bad_group(N, g) || B < 1 || B > kMaxB ||
-      too_big(K, M, N, B) || (size_t)K * M * (N / g) >= (1u << 30))
+  if (K < 1 || K > 4 || M < 0 || bad_n(N) || bad_group(N, g) || (s != 0 && bad_salient(s)) || B < 1 ||
+      B > kMaxB || too_big(K, M, N, B) || (size_t)K * M * (N / g) >= (1u << 30))
     return BSG_ERR_SHAPE;
+  // the salient tables share the main tables' space: column scales on both branches or on neither
+  if (s && (colscale != nullptr) != (scolscale != nullptr)) return BSG_ERR_SHAPE;
   if (M == 0) return BSG_OK;
   if (!bits || !alpha || !x || !y) return BSG_ERR_NULL;
-  if (misaligned(bits, 16) || misaligned(alpha, 4) || misaligned(colscale, 2) ||
-      misaligned(x, dtype_size(x_dtype)) || misaligned(y, 4))
+  if (s && (!sbits || !idx || !salpha)) return BSG_ERR_NULL;
+  if (misaligned(bits, 16) || misaligned(alpha, 2) || misaligned(colscale, 2) ||
+      misaligned(x, dtype_size(x_dtype)) || misaligned(y, 4) || misaligned(sbits, 16) || misaligned(idx, 16) ||
+      misaligned(salpha, 8) || misaligned(scolscale, 8))
     return BSG_ERR_ALIGN;
   ProdArgs a{};
   a.bits = bits;
-  a.alpha = alpha;
+  a.alpha = (const float*)(const void*)alpha;  // fp16 scales, read as such by the grouped kernels
   a.colscale = colscale;
   a.x = x;
   a.y = y;
@@ -320,7 +343,24 @@ bsg_status bs_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, con
   a.xvec = xvec_ok(x, colscale);
   a.gsw = g / 32;
   a.ngrp = N / g;
+  if (s) {
+    a.vs_bits = sbits;
+    a.vs_S = salient_cols(N, g, s);
+    a.vs_nd = salient_words(N, g, s);
+    a.vs_plane = plane_words(M, a.vs_nd);
+    a.vs_idx = idx;
+    a.vs_alpha = salpha;
+    a.vs_cs = scolscale;
+    a.vs_gpw = 32 / s;
+  }
   return hip_status(launch_prod_grouped(a, (hipStream_t)stream));
+}
+
+bsg_status bs_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, const uint16_t* alpha,
+                           const uint16_t* colscale, const void* x, int x_dtype, int B, float* y, int accumulate,
+                           void* stream) {
+  return bs_gemv_hybrid(bits, K, M, N, g, alpha, colscale, nullptr, 0, nullptr, nullptr, nullptr, x, x_dtype, B, y,
+                        accumulate, stream);
 }
 
 size_t binlr_fit_workspace_bytes(int M, int N, int r) {

@@ -1,11 +1,15 @@
 // Binary-base product with group-wise row scales (FluxBin Sec. 3.1: one row
-// scale per weight group; g = 128 in its Kb-g128 configurations):
+// scale per weight group; g = 128 in its Kb-g128 configurations; App. C.2:
+// scales stored in fp16), optionally with the salient-column bases of its
+// hybrid configurations read through the Virtual Columnar Mapping (Sec. 3.2):
 //
 //   y[m,b] (= or +=) sum_k sum_j alpha_k[m][j] sum_{n in group j} (2 bit_k(m,n) - 1) c_k[n] x[n,b]
+//                  + sum_k sum_j salpha_k[m][j] sum_{i < s} (2 sbit_k(m, js+i) - 1) sc_k[js+i] x[idx[js+i],b]
 //
 // The table kernel of bsg_prod_f.h with GS = 1: every lane sums its words of
 // a chunk apart (they lie in one group) and adds that sum times its group's
-// scale.  One batch column per launch.
+// scale; the salient chunks follow the main ones.  One batch column per
+// launch.
 #include "bsg_prod_f.h"
 
 namespace bsg {
@@ -18,10 +22,14 @@ namespace bsg {
   BSG_PROD_XM(X, 2, 4, 3) BSG_PROD_XM(X, 2, 4, 4) BSG_PROD_XM(X, 4, 1, 3) BSG_PROD_XM(X, 4, 1, 4)            \
   BSG_PROD_XM(X, 2, 2, 3) BSG_PROD_XM(X, 2, 2, 4) BSG_PROD_XM(X, 1, 4, 3) BSG_PROD_XM(X, 1, 4, 4)
 
+// GS = 2: with the salient-column bases
 static hipError_t dispatch_gs(const ProdArgs& a, const ProdPlan& p, hipStream_t st) {
+  const bool sal = a.vs_bits != nullptr;
   switch (prod_key(p.Q, p.NWL, p.KM, p.BB, p.XM)) {
-#define BSG_CASE(Q, NWL, KM, BB, XM) \
-  case prod_key(Q, NWL, KM, BB, XM): return launch_one(k_prod_f<Q, NWL, KM, BB, XM, 0, 1>, p, a, st);
+#define BSG_CASE(Q, NWL, KM, BB, XM)                                                           \
+  case prod_key(Q, NWL, KM, BB, XM):                                                           \
+    return sal ? launch_one(k_prod_f<Q, NWL, KM, BB, XM, 0, 2>, p, a, st)                      \
+               : launch_one(k_prod_f<Q, NWL, KM, BB, XM, 0, 1>, p, a, st);
     BSG_PROD_GS_INSTANCES(BSG_CASE)
 #undef BSG_CASE
     default: return hipErrorInvalidConfiguration;
@@ -34,8 +42,16 @@ hipError_t launch_prod_grouped(const ProdArgs& a0, hipStream_t st) {
   ProdArgs as = a0;
   as.x_bytes = (uint32_t)((size_t)a0.N * a0.B * (a0.xdt == BSG_F32 ? 4 : 2));
   as.cs_bytes = a0.colscale ? (uint32_t)((size_t)a0.K * a0.N * 2) : 0u;
-  as.al_bytes = (uint32_t)((size_t)a0.K * a0.M * a0.ngrp * 4);
+  as.al_bytes = (uint32_t)((size_t)a0.K * a0.M * a0.ngrp * 2);
   p.XM = (a0.B == 1 && a0.xvec && a0.xdt != BSG_F32) ? (a0.xdt == BSG_BF16 ? 1 : 2) : 0;
+  // the instance for this XM may allow fewer wavefronts than the plan took
+  const int wmax = prod_max_waves(p.KM, p.BB, a0.vs_bits ? 2 : 1, p.XM);
+  if (p.W > wmax) {
+    const int T = (a0.ND + p.CW - 1) / p.CW;
+    p.lds = p.lds / p.W * wmax;
+    p.W = wmax;
+    p.NCH = (T + p.W - 1) / p.W;
+  }
   for (int c = 0; c < p.nlaunch; ++c) {
     ProdArgs a = as;
     a.b0 = c;

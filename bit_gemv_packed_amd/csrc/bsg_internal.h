@@ -102,7 +102,17 @@ struct ProdArgs {
   // that the kernel prologue has no branches
   uint32_t x_bytes, cs_bytes, al_bytes;
   int xvec;                  // x 16-byte and colscale 8-byte aligned: vector loads
-  int gsw, ngrp;             // group-wise row scales: sign words per group, groups per row
+  int gsw, ngrp;             // group-wise row scales (fp16 [K][ngrp][M] at alpha): words per group, groups
+  // Salient columns of the group-wise path (FluxBin VCM; NULL vs_bits when
+  // absent): K bases over vs_S physical columns p, column p reading x[vs_idx[p]];
+  // fp16 row scales word-grouped, vs_gpw per sign word: (k, w, m, t) at
+  // ((k * vs_nd + w) * M + m) * vs_gpw + t; fp16 column scales [K][vs_S]
+  const uint32_t* vs_bits;
+  size_t vs_plane;
+  const int32_t* vs_idx;
+  const uint16_t* vs_alpha;
+  const uint16_t* vs_cs;
+  int vs_S, vs_nd, vs_gpw;
   // int8 path
   const int8_t* xq;          // [N][B]
   const float* sx;           // [B]
@@ -128,7 +138,8 @@ struct ProdArgs {
 hipError_t launch_prod_f(const ProdArgs& a, const ProdPlan& p, hipStream_t s);
 // One launch over a.np > 1 projections (a.proj) sharing x (bsg_gemv.hip).
 hipError_t launch_prod_multi(const ProdArgs& a, hipStream_t s);
-// Group-wise row scales (bsg_gemv_gs.hip): a.gsw, a.ngrp set, alpha [K][M][ngrp].
+// Group-wise row scales (bsg_gemv_gs.hip): a.gsw, a.ngrp set, alpha fp16 [K][ngrp][M];
+// optional salient columns (a.vs_*).
 hipError_t launch_prod_grouped(const ProdArgs& a, hipStream_t s);
 // Batched product on the matrix cores (bsg_gemv_mfma.hip): B >= 4 columns of
 // bf16 / fp16 x, no column scales.

@@ -23,12 +23,10 @@ __global__ void k_widen(const float* __restrict__ W, double* __restrict__ R, siz
 
 // mode 0: out[m] = fp32(sum_n |R[m,n]| / N)                (row scale)
 // mode 1: outd[m] = sum_n |W[m,n]| * xbar[n]  (W fp32)      (protected-row score)
-// mode 2: out[j * M + m] = fp32(sum_{n in group j} |R[m,n]| / g)
-//         (group-wise row scales, group-major; g a multiple of the 64-column tile)
 template <int MODE>
 __global__ void __launch_bounds__(kT) k_rowsum(const double* __restrict__ R, const float* __restrict__ W,
                                               const float* __restrict__ xbar, int M, int N,
-                                              float* __restrict__ out, double* __restrict__ outd, int g) {
+                                              float* __restrict__ out, double* __restrict__ outd) {
   __shared__ double tile[kT][kT + 1];
   const int t = threadIdx.x;
   const int m0 = blockIdx.x * kT;
@@ -39,7 +37,7 @@ __global__ void __launch_bounds__(kT) k_rowsum(const double* __restrict__ R, con
       const int m = m0 + i;
       double v = 0.0;
       if (m < M && n < N) {
-        if (MODE != 1) {
+        if (MODE == 0) {
           v = fabs(R[(size_t)m * N + n]);
         } else {
           v = fabs((double)W[(size_t)m * N + n]) * (double)xbar[n];
@@ -51,11 +49,6 @@ __global__ void __launch_bounds__(kT) k_rowsum(const double* __restrict__ R, con
     const int lim = min(kT, N - n0);
     for (int j = 0; j < lim; ++j) acc = acc + tile[t][j];
     __syncthreads();
-    if (MODE == 2 && (n0 + kT) % g == 0) {  // end of group (n0 + kT) / g - 1
-      const int m = m0 + t;
-      if (m < M) out[(size_t)((n0 + kT) / g - 1) * M + m] = (float)(acc / (double)g);
-      acc = 0.0;
-    }
   }
   const int m = m0 + t;
   if (m < M) {
@@ -65,17 +58,18 @@ __global__ void __launch_bounds__(kT) k_rowsum(const double* __restrict__ R, con
 }
 
 // Sign bits of a row-major real matrix (fp64 residual or fp32 input) into
-// the device layout: one wavefront per row, one ballot per 64 columns.
+// the device layout: one wavefront per row, one ballot per 64 columns.  NC
+// columns (the row stride), ND >= NC / 32 words per row; bits at or beyond
+// NC are clear.
 template <typename T>
-__global__ void __launch_bounds__(64) k_signs(const T* __restrict__ R, int M, int N, uint32_t* __restrict__ bits,
-                                             size_t plane, int k) {
+__global__ void __launch_bounds__(64) k_signs(const T* __restrict__ R, int M, int NC, int ND,
+                                             uint32_t* __restrict__ bits, size_t plane, int k) {
   // one workgroup per padded row: every word of the row, padding included
   const int m = blockIdx.x;
-  const int ND = N / 32;
   const int NP = pad_words(ND) * 32;
   for (int n0 = 0; n0 < NP; n0 += 64) {
     const int n = n0 + threadIdx.x;
-    const bool pos = m < M && n < N && R[(size_t)m * N + n] >= (T)0;
+    const bool pos = m < M && n < NC && R[(size_t)m * NC + n] >= (T)0;
     const unsigned long long b = __ballot(pos);
     if (threadIdx.x == 0) {
       const int w = n0 / 32;  // even; w + 1 < NP / 32
@@ -125,21 +119,51 @@ __global__ void k_residual(double* __restrict__ R, const float* __restrict__ alp
   }
 }
 
-// Group-wise row scales alpha [G][M] (G = N / g, group-major): den[j] = sum_m alpha[m][j]^2,
-// cs[n] = fp16(fp32(sum_m alpha[m][j] |R[m,n]| / den[j])) for the group j of
-// n (1 when den[j] == 0), and the residual update with alpha[m][j(n)].
-__global__ void k_den_grouped(const float* __restrict__ alpha, int M, int G, double* __restrict__ den) {
+// Group-wise row scales in fp16 (one per row and group of g consecutive
+// columns of a residual R [M][NC]; G = NC / g groups), stored word-grouped:
+// the gpw = max(1, 32 / g) scales of one 32-column word of a row are
+// adjacent, rows consecutive, i.e. scale (m, j) at scale_index(...).
+__device__ inline size_t scale_index(int M, int gpw, int m, int j) {
+  return ((size_t)(j / gpw) * M + m) * gpw + j % gpw;
+}
+
+// a[m][j] = fp16(fp32(sum_{n in group j} |R[m,n]| / g)), ascending n; the
+// slots of a last partly used word (j >= G) get 0
+__global__ void k_gscale(const double* __restrict__ R, int M, int NC, int g, int gpw, uint16_t* __restrict__ a) {
+  const int G = NC / g, GS = (G + gpw - 1) / gpw * gpw;
+  const size_t total = (size_t)M * GS;
+  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
+    const int m = (int)(t % M), j = (int)(t / M);
+    uint16_t hb = 0;
+    if (j < G) {
+      const double* r = R + (size_t)m * NC + (size_t)j * g;
+      double s = 0.0;
+      for (int i = 0; i < g; ++i) s = s + fabs(r[i]);
+      const _Float16 h = (_Float16)(float)(s / (double)g);
+      __builtin_memcpy(&hb, &h, 2);
+    }
+    a[scale_index(M, gpw, m, j)] = hb;
+  }
+}
+
+// den[j] = sum_m a[m][j]^2, ascending m
+__global__ void k_gden(const uint16_t* __restrict__ a, int M, int G, int gpw, double* __restrict__ den) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= G) return;
   double s = 0.0;
-  for (int m = 0; m < M; ++m) s = s + (double)alpha[(size_t)j * M + m] * (double)alpha[(size_t)j * M + m];
+  for (int m = 0; m < M; ++m) {
+    const double v = (double)f16_bits_to_float(a[scale_index(M, gpw, m, j)]);
+    s = s + v * v;
+  }
   den[j] = s;
 }
 
-__global__ void k_colscale_grouped(const double* __restrict__ R, const float* __restrict__ alpha,
-                                   const double* __restrict__ den, int M, int N, int g, uint16_t* __restrict__ cs) {
+// cs[n] = fp16(fp32(sum_m a[m][j] |R[m,n]| / den[j])) for the group j of n
+// (1 when den[j] == 0)
+__global__ void k_gcolscale(const double* __restrict__ R, const uint16_t* __restrict__ a,
+                            const double* __restrict__ den, int M, int NC, int g, int gpw, uint16_t* __restrict__ cs) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
+  if (n >= NC) return;
   const int j = n / g;
   const double d = den[j];
   uint16_t h;
@@ -147,25 +171,37 @@ __global__ void k_colscale_grouped(const double* __restrict__ R, const float* __
     h = 0x3c00u;
   } else {
     double num = 0.0;
-    for (int m = 0; m < M; ++m) num = num + (double)alpha[(size_t)j * M + m] * fabs(R[(size_t)m * N + n]);
-    const float c32 = (float)(num / d);
-    const _Float16 c16 = (_Float16)c32;
+    for (int m = 0; m < M; ++m)
+      num = num + (double)f16_bits_to_float(a[scale_index(M, gpw, m, j)]) * fabs(R[(size_t)m * NC + n]);
+    const _Float16 c16 = (_Float16)(float)(num / d);
     __builtin_memcpy(&h, &c16, 2);
   }
   cs[n] = h;
 }
 
-__global__ void k_residual_grouped(double* __restrict__ R, const float* __restrict__ alpha,
-                                   const uint16_t* __restrict__ cs, int M, int N, int g) {
-  const size_t total = (size_t)M * N;
+// R <- R - a[m][j(n)] c[n] (2 bit - 1), the sign being that of R itself
+__global__ void k_gresidual(double* __restrict__ R, const uint16_t* __restrict__ a, const uint16_t* __restrict__ cs,
+                            int M, int NC, int g, int gpw) {
+  const size_t total = (size_t)M * NC;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const int m = (int)(i / N);
-    const int n = (int)(i % N);
+    const int m = (int)(i / NC);
+    const int n = (int)(i % NC);
     const double r = R[i];
     const double sgn = r >= 0.0 ? 1.0 : -1.0;
     const double c = cs ? (double)f16_bits_to_float(cs[n]) : 1.0;
-    const double t = (double)alpha[(size_t)(n / g) * M + m] * c;
+    const double t = (double)f16_bits_to_float(a[scale_index(M, gpw, m, n / g)]) * c;
     R[i] = r - t * sgn;
+  }
+}
+
+// Rs[m][p] = R[m][idx[p]] (0 for an index outside [0, N))
+__global__ void k_gather_cols(const double* __restrict__ R, int M, int N, const int32_t* __restrict__ idx, int S,
+                              double* __restrict__ Rs) {
+  const size_t total = (size_t)M * S;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i / S);
+    const int n = idx[i % S];
+    Rs[i] = (n >= 0 && n < N) ? R[(size_t)m * N + n] : 0.0;
   }
 }
 
@@ -279,9 +315,9 @@ hipError_t launch_pack(const float* W, int M, int N, int K, bool colscale, uint3
   for (int k = 0; k < K; ++k) {
     float* ak = alpha + (size_t)k * M;
     uint16_t* ck = colscale ? cs + (size_t)k * N : nullptr;
-    hipLaunchKernelGGL(k_signs<double>, dim3(pad_rows(M)), dim3(64), 0, st, R, M, N, bits, plane, k);
+    hipLaunchKernelGGL(k_signs<double>, dim3(pad_rows(M)), dim3(64), 0, st, R, M, N, N / 32, bits, plane, k);
     hipLaunchKernelGGL(k_rowsum<0>, dim3((M + kT - 1) / kT), dim3(kT), 0, st, R, (const float*)nullptr,
-                       (const float*)nullptr, M, N, ak, (double*)nullptr, 0);
+                       (const float*)nullptr, M, N, ak, (double*)nullptr);
     if (colscale) {
       hipLaunchKernelGGL(k_den, dim3(1), dim3(64), 0, st, ak, M, den);
       hipLaunchKernelGGL(k_colscale, dim3((N + 255) / 256), dim3(256), 0, st, R, ak, den, M, N, ck);
@@ -293,34 +329,50 @@ hipError_t launch_pack(const float* W, int M, int N, int K, bool colscale, uint3
   return hipSuccess;
 }
 
-hipError_t launch_pack_grouped(const float* W, int M, int N, int K, int g, bool colscale, uint32_t* bits,
-                               float* alpha, uint16_t* cs, void* ws, hipStream_t st) {
-  double* R = (double*)ws;
-  double* den = (double*)((char*)ws + align_up((size_t)M * N * 8, 256));
-  const size_t mn = (size_t)M * N;
-  const int ND = N / 32, G = N / g;
-  const size_t plane = plane_words(M, ND);
-  hipLaunchKernelGGL(k_widen, dim3(grid_for(mn, 256)), dim3(256), 0, st, W, R, mn);
+// K greedy bases with fp16 group scales on the residual R [M][NC] (groups of
+// g columns, scales word-grouped with gpw per word); updates R after every
+// base but the last unless update_last.
+static hipError_t grouped_bases(double* R, int M, int NC, int ND, int g, int gpw, int K, uint32_t* bits,
+                                uint16_t* alpha, uint16_t* cs, double* den, bool update_last, hipStream_t st) {
+  const size_t mn = (size_t)M * NC;
+  const int G = NC / g, GS = (G + gpw - 1) / gpw * gpw;
+  const size_t plane = plane_words(M, ND), aplane = (size_t)GS * M;
   for (int k = 0; k < K; ++k) {
-    float* ak = alpha + (size_t)k * M * G;
-    uint16_t* ck = colscale ? cs + (size_t)k * N : nullptr;
-    hipLaunchKernelGGL(k_signs<double>, dim3(pad_rows(M)), dim3(64), 0, st, R, M, N, bits, plane, k);
-    hipLaunchKernelGGL(k_rowsum<2>, dim3((M + kT - 1) / kT), dim3(kT), 0, st, R, (const float*)nullptr,
-                       (const float*)nullptr, M, N, ak, (double*)nullptr, g);
-    if (colscale) {
-      hipLaunchKernelGGL(k_den_grouped, dim3((G + 255) / 256), dim3(256), 0, st, ak, M, G, den);
-      hipLaunchKernelGGL(k_colscale_grouped, dim3((N + 255) / 256), dim3(256), 0, st, R, ak, den, M, N, g, ck);
+    uint16_t* ak = alpha + (size_t)k * aplane;
+    uint16_t* ck = cs ? cs + (size_t)k * NC : nullptr;
+    hipLaunchKernelGGL(k_signs<double>, dim3(pad_rows(M)), dim3(64), 0, st, R, M, NC, ND, bits, plane, k);
+    hipLaunchKernelGGL(k_gscale, dim3(grid_for((size_t)M * GS, 256)), dim3(256), 0, st, R, M, NC, g, gpw, ak);
+    if (cs) {
+      hipLaunchKernelGGL(k_gden, dim3((G + 255) / 256), dim3(256), 0, st, ak, M, G, gpw, den);
+      hipLaunchKernelGGL(k_gcolscale, dim3((NC + 255) / 256), dim3(256), 0, st, R, ak, den, M, NC, g, gpw, ck);
     }
-    if (k + 1 < K)
-      hipLaunchKernelGGL(k_residual_grouped, dim3(grid_for(mn, 256)), dim3(256), 0, st, R, ak, ck, M, N, g);
+    if (k + 1 < K || update_last)
+      hipLaunchKernelGGL(k_gresidual, dim3(grid_for(mn, 256)), dim3(256), 0, st, R, ak, ck, M, NC, g, gpw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+hipError_t launch_pack_hybrid(const float* W, int M, int N, int K, int g, int s, const int32_t* idx, bool colscale,
+                              uint32_t* bits, uint16_t* alpha, uint16_t* cs, uint32_t* sbits, uint16_t* salpha,
+                              uint16_t* scs, void* ws, hipStream_t st) {
+  const int G = N / g, S = s * G;
+  double* R = (double*)ws;
+  double* Rs = (double*)((char*)ws + align_up((size_t)M * N * 8, 256));
+  double* den = (double*)((char*)Rs + align_up((size_t)M * S * 8, 256));
+  const size_t mn = (size_t)M * N;
+  hipLaunchKernelGGL(k_widen, dim3(grid_for(mn, 256)), dim3(256), 0, st, W, R, mn);
+  hipError_t e = grouped_bases(R, M, N, N / 32, g, 1, K, bits, alpha, colscale ? cs : nullptr, den, s > 0, st);
+  if (e != hipSuccess || s == 0) return e;
+  hipLaunchKernelGGL(k_gather_cols, dim3(grid_for((size_t)M * S, 256)), dim3(256), 0, st, R, M, N, idx, S, Rs);
+  return grouped_bases(Rs, M, S, (S + 31) / 32, s, s < 32 ? 32 / s : 1, K, sbits, salpha, colscale ? scs : nullptr,
+                       den, false, st);
+}
+
 hipError_t launch_pack_signs(const float* S, int M, int N, uint32_t* bits, hipStream_t st) {
-  hipLaunchKernelGGL(k_signs<float>, dim3(pad_rows(M)), dim3(64), 0, st, S, M, N, bits, plane_words(M, N / 32), 0);
+  hipLaunchKernelGGL(k_signs<float>, dim3(pad_rows(M)), dim3(64), 0, st, S, M, N, N / 32, bits, plane_words(M, N / 32),
+                     0);
   return hipGetLastError();
 }
 
@@ -334,7 +386,7 @@ hipError_t launch_salient(const float* W, int M, int N, const float* xbar, int n
   double* score = (double*)ws;
   int* sel = (int*)((char*)ws + align_up((size_t)M * 8, 256));
   hipLaunchKernelGGL(k_rowsum<1>, dim3((M + kT - 1) / kT), dim3(kT), 0, st, (const double*)nullptr, W, xbar, M, N,
-                     (float*)nullptr, score, 0);
+                     (float*)nullptr, score);
   hipLaunchKernelGGL(k_rank, dim3((M + 255) / 256), dim3(256), 0, st, score, M, ns, sel);
   hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, sel, M, ns, rows);
   if (ns > 0) hipLaunchKernelGGL(k_quant_rows, dim3(ns), dim3(256), 0, st, W, M, N, rows, q, s, alpha, K);

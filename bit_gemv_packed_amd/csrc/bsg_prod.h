@@ -124,9 +124,12 @@ __device__ inline void wave_sync() {
 
 // Most wavefronts per workgroup of an instance: 16, or 8 where KM * BB >= 8
 // partial sums (and as many sign-word sets) live in registers, or four bases
-// carry group scales as well, so that the kernel has up to 256 VGPRs and
-// does not spill.
-constexpr int prod_max_waves(int KM, int BB, int GS = 0) { return (KM * BB >= 8 || (GS && KM >= 4)) ? 8 : 16; }
+// carry group scales as well, or three do with the generic activation path
+// (XM = 0; XM < 0: not yet chosen), so that the kernel has up to 256 VGPRs
+// and does not spill.
+constexpr int prod_max_waves(int KM, int BB, int GS = 0, int XM = -1) {
+  return (KM * BB >= 8 || (GS && KM >= 4) || (GS && KM >= 3 && XM == 0)) ? 8 : 16;
+}
 
 // Sum of the W <= 16 per-wavefront partials p[0], p[stride], ... read from
 // LDS all at once (straight-line), added in a fixed order.

@@ -33,6 +33,7 @@
 #include "bsg_prod.h"
 
 #include <cstdlib>
+#include <type_traits>
 
 namespace bsg {
 
@@ -221,6 +222,66 @@ __device__ __forceinline__ void lookup_chunk(const ProdArgs& a, const char* lds,
   }
 }
 
+// Activations of one 4-column group of the salient matrix (FluxBin Sec. 3.2
+// Virtual Columnar Mapping): physical columns p0 .. p0 + 3 read x at the
+// logical columns idx[p0 + j] (an index outside [0, N) reads 0), with the
+// salient column scales (8-byte aligned: one load per base); the raw form of
+// fetch_act's generic path, one load per element.  iv: the four indices.
+template <int KM, int BB>
+__device__ __forceinline__ void fetch_gather(const ProdArgs& a, const ActSrc& src, uint4 iv, int n_true, int p0,
+                                             ActRaw<KM, BB>& r) {
+  const uint32_t id[4] = {iv.x, iv.y, iv.z, iv.w};
+  const uint32_t esz = src.xdt == BSG_F32 ? 4u : 2u;
+#pragma unroll
+  for (int b = 0; b < BB; ++b) {
+    const int bb = src.b0 + b < src.B ? src.b0 + b : src.B - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t off = id[j] < (uint32_t)n_true ? (id[j] * (uint32_t)src.B + (uint32_t)bb) * esz : 0xfffffff0u;
+      r.x[b][j] = esz == 4 ? ld32(src.x, off) : ld16(src.x, off);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KM; ++k)
+    if (base_active<KM>(a, k)) r.c[k] = ld64(src.c, (uint32_t)(k * src.N + p0) * 2u);
+}
+
+// Lookups of one salient chunk: like lookup_chunk, but each 4-bit slice's
+// entry is scaled by the fp16 row scale of its group (GPW groups per word:
+// slice n of a word lies in group n * GPW / 8), sc[k][j] holding word j's
+// GPW scales (two per 32-bit value).
+template <int Q, int NWL, int KM, int GPW>
+__device__ __forceinline__ void lookup_chunk_scaled(const ProdArgs& a, const char* lds, uint32_t wbase_lds, bool cs,
+                                                    int q, const uint32_t (&cur)[KM][NWL],
+                                                    const uint2 (&sc)[KM][NWL], float (&acc)[KM]) {
+  constexpr uint32_t ROWB = Q * 64 + 16;
+  constexpr uint32_t REG = NWL * 8 * ROWB;
+#pragma unroll
+  for (int j = 0; j < NWL; ++j) {
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (base_active<KM>(a, k)) {
+        const uint32_t lbase = (uint32_t)(uintptr_t)(lds + wbase_lds + (uint32_t)(cs ? k : 0) * REG + (uint32_t)q * 64);
+        const uint32_t word = cur[k][j];
+        const uint32_t rl = __builtin_amdgcn_alignbit(word, word, 30) & 0x3c3c3c3cu;
+        const uint32_t rr = __builtin_amdgcn_alignbit(word, word, 2) & 0x3c3c3c3cu;
+        const uint32_t ad[8] = {byte_add<0>(lbase, rl), byte_add<0>(lbase, rr), byte_add<1>(lbase, rl),
+                                byte_add<1>(lbase, rr), byte_add<2>(lbase, rl), byte_add<2>(lbase, rr),
+                                byte_add<3>(lbase, rl), byte_add<3>(lbase, rr)};
+        float f[GPW];
+#pragma unroll
+        for (int t = 0; t < GPW; ++t) {
+          const uint32_t w2 = t < 2 ? sc[k][j].x : sc[k][j].y;
+          f[t] = f16_bits_to_float((uint16_t)((t & 1) ? (w2 >> 16) : w2));
+        }
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+          acc[k] = __builtin_fmaf(f[n * GPW / 8], lds_f32(ad[n] + (uint32_t)(j * 8 + n) * ROWB), acc[k]);
+      }
+    }
+  }
+}
+
 // First index i in [0, n) with rows[i] >= key (n if none), rows ascending:
 // a 64-way search, one probe per lane per round, so about log64(n) + 1
 // dependent loads.  Uniform over the wavefront.
@@ -247,13 +308,14 @@ __device__ __forceinline__ int lower_bound_rows(rsrc_t rows, int n, int key, int
 // more registers and is not held).  Instances with KM * BB >= 8 keep more
 // sums in registers and run at most 8 wavefronts per workgroup.
 // MP = 1: the fused launch of several projections (bs_gemv_multi); the
-// single-product instances (MP = 0) carry none of its code.  GS = 1: one row
+// single-product instances (MP = 0) carry none of its code.  GS >= 1: one row
 // scale per group of a.gsw sign words (FluxBin Sec. 3.1, group-wise row
 // scales): each lane's words of a chunk lie in one group, so the lane sums
 // a chunk apart and adds it times its group's scales, which are loaded with
-// the chunk's sign words (two chunks ahead, in three buffers).
+// the chunk's sign words (two chunks ahead, in three buffers).  GS = 2 adds
+// the salient-column bases.
 template <int Q, int NWL, int KM, int BB, int XM, int MP, int GS = 0>
-__global__ void __launch_bounds__(64 * prod_max_waves(KM, BB, GS), (KM <= 2 && BB == 1 && Q >= 2 && XM != 0 && !GS) ? 8 : 1)
+__global__ void __launch_bounds__(64 * prod_max_waves(KM, BB, GS, XM), (KM <= 2 && BB == 1 && Q >= 2 && XM != 0 && !GS) ? 8 : 1)
     k_prod_f(ProdArgs a) {
   constexpr int RW = 64 / Q;
   constexpr int CW = Q * NWL;
@@ -334,12 +396,53 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB, GS), (KM <= 2 && B
 #pragma unroll
     for (int k = 0; k < KM; ++k)
       if (base_active<KM>(a, k))
-        d[k] = __uint_as_float(ld32(alsrc, (uint32_t)((k * a.ngrp + j) * a.M + m) * 4u));
+        d[k] = f16_bits_to_float((uint16_t)ld16(alsrc, (uint32_t)((k * a.ngrp + j) * a.M + m) * 2u));
   };
   load_chunk<KM, NWL>(a, srows, c0 * CW + q * NWL, wb0);
   if (GS) load_gscale(0, ab0);
   load_chunk<KM, NWL>(a, srows, (c0 + min(1, clast)) * CW + q * NWL, wb1);
   if (GS) load_gscale(min(1, clast), ab1);
+
+  // Salient columns (GS = 2; FluxBin Sec. 3.1 hybrid bases, Sec. 3.2 Virtual
+  // Columnar Mapping): K more bases over the dense physical matrix of the
+  // gathered columns, after the main chunks.  Its chunks go to the
+  // wavefronts from the last one down (the last may have fewer main chunks).
+  // (Gathering the first salient chunk's activations here instead, behind
+  // the main chunks' first loads, measured slower: the gather waits for the
+  // index list and with it for every load issued before.)
+  const int vc0 = (int)a.W - 1 - wv;  // this wavefront's first salient chunk
+  const int nds = a.vs_nd;
+  const SignRows<KM> vrows = sign_rows<KM, RW>(a.vs_bits, a.vs_plane, a.K, nds, blk, m);
+  ActSrc ss = asrc;
+  ss.N = a.vs_S;
+  ss.c = make_rsrc(a.vs_cs, a.vs_cs ? (size_t)a.K * a.vs_S * 2 : 0);
+  ss.cs = a.vs_cs != nullptr;
+  const rsrc_t ir = make_rsrc(a.vs_idx, (size_t)a.vs_S * 4);
+  const rsrc_t sar = make_rsrc(a.vs_alpha, (size_t)a.K * nds * a.M * a.vs_gpw * 2);
+  // the gathered activations, sign words and row scales of salient chunk cu
+  auto salient_gather = [&](int cu, ActRaw<KM, BB>(&ga)[GPL]) {
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int p0 = cu * CW * 32 + grp(i) * 4;
+      fetch_gather<KM, BB>(a, ss, ld128(ir, (uint32_t)p0 * 4u), a.N, p0, ga[i]);
+    }
+  };
+  auto salient_words = [&](int cu, uint32_t(&sw)[KM][NWL], uint2(&sc)[KM][NWL]) {
+    load_chunk<KM, NWL>(a, vrows, cu * CW + q * NWL, sw);
+    const int gpw = a.vs_gpw;
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+#pragma unroll
+      for (int j = 0; j < NWL; ++j) {
+        if (base_active<KM>(a, k)) {
+          const uint32_t off = (uint32_t)(((k * nds + cu * CW + q * NWL + j) * a.M + m) * gpw) * 2u;
+          if (gpw == 4) sc[k][j] = ld64(sar, off);
+          else if (gpw == 2) sc[k][j] = make_uint2(ld32(sar, off), 0u);
+          else sc[k][j] = make_uint2(ld16(sar, off), 0u);
+        }
+      }
+    }
+  };
 
   // one chunk: build its tables, issue the next chunk's activations and the
   // sign words two chunks ahead (into `ahead`), look up `cur`
@@ -425,6 +528,39 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB, GS), (KM <= 2 && B
     }
 #pragma unroll
     for (int b = 0; b < BB; ++b) tot[b] += lacc[0][b];
+  }
+
+  // ---- the salient chunks (GS = 2)
+  if (GS == 2) {
+    const int KS = ss.cs ? a.K : 1;
+    const int ts = (nds + CW - 1) / CW;
+    float sacc[KM];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) sacc[k] = 0.0f;
+    auto pass = [&](auto gpw_c) {
+      constexpr int GPW = decltype(gpw_c)::value;
+      for (int cu = vc0; cu < ts; cu += a.W) {
+        ActRaw<KM, BB> ga[GPL];
+        uint32_t sw[KM][NWL];
+        uint2 sc[KM][NWL];
+        salient_words(cu, sw, sc);
+        salient_gather(cu, ga);
+        wave_sync();  // earlier lookups of this wavefront's tables are done
+#pragma unroll
+        for (int i = 0; i < GPL; ++i)
+          if (lane + 64 * i < G)
+            build_tables<Q, NWL, KM, BB, 0>(ss, ga[i], KS, lane + 64 * i, cu * CW * 32 + (lane + 64 * i) * 4, lds,
+                                            wbase_lds);
+        wave_sync();
+        lookup_chunk_scaled<Q, NWL, KM, GPW>(a, lds, wbase_lds, ss.cs, q, sw, sc, sacc);
+      }
+    };
+    if (a.vs_gpw == 4) pass(std::integral_constant<int, 4>());
+    else if (a.vs_gpw == 2) pass(std::integral_constant<int, 2>());
+    else pass(std::integral_constant<int, 1>());
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (base_active<KM>(a, k)) tot[0] += sacc[k];
   }
 
   // ---- fused protected rows: y[rows[i]] += s_i (q_i . x) (BiSCo-LLM,

@@ -220,38 +220,83 @@ BSG_API bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const floa
 /*
  * bsq_pack_grouped -- bsq_pack with one row scale per row and per group of g
  * consecutive columns (FluxBin Sec. 3.1: a row scale per weight group;
- * g = 128 in its Kb-g128 configurations):
- *   alpha_k[m][j] = fp32( sum_{n in group j} |R[m,n]| / g )
- *   c_k[n] = fp16(fp32( sum_m alpha_k[m][j] |R[m,n]| / sum_m alpha_k[m][j]^2 ))
- *            for the group j of column n (BSG_PACK_COLSCALE; 1 when the
- *            denominator is 0)
- *   R <- R - alpha_k[m][j(n)] c_k[n] B_k[m,n]
- *   alpha     (device) out: fp32 [K][N/g][M], group-major (alpha_k[m][j] at
+ * g = 128 in its Kb-g128 configurations; App. C.2: scales stored in fp16):
+ *   alpha_k[m][j] = fp16(fp32( sum_{n in group j} |R[m,n]| / g ))
+ *   c_k[n] = fp16(fp32( sum_m a_k[m][j] |R[m,n]| / sum_m a_k[m][j]^2 ))
+ *            with a the stored fp16 scales of the group j of column n
+ *            (BSG_PACK_COLSCALE; 1 when the denominator is 0)
+ *   R <- R - a_k[m][j(n)] c_k[n] B_k[m,n]
+ *   alpha     (device) out: fp16 [K][N/g][M], group-major (alpha_k[m][j] at
  *             (k * (N/g) + j) * M + m: the scales of one group are contiguous
  *             over the rows, so a wavefront's rows read them in one access)
  *   other arguments as bsq_pack; workspace >= bsq_pack_grouped_workspace_bytes.
- * g a power of two >= 64 dividing N (N % 32 == 0).  g = N gives bsq_pack's
- * result.  fp64 sums in ascending order: bit-exact with a sequential
- * double-precision implementation of the recipe.
+ * g a power of two >= 64 dividing N (N % 32 == 0).  fp64 sums in ascending
+ * order: bit-exact with a sequential double-precision implementation of the
+ * recipe.  Same as bsq_pack_hybrid with s = 0.
  */
 BSG_API size_t bsq_pack_grouped_workspace_bytes(int M, int N, int g);
 BSG_API bsg_status bsq_pack_grouped(const float* W, int M, int N, int K, int g, int flags, uint32_t* bits,
-                                    float* alpha, uint16_t* colscale, void* workspace, size_t workspace_bytes,
+                                    uint16_t* alpha, uint16_t* colscale, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * bsq_pack_hybrid -- bsq_pack_grouped plus K salient-column bases (FluxBin
+ * Sec. 3.1 "Structural Saliency Search": hybrid bases, extra bases on s
+ * salient columns per group of g; Sec. 3.2 Virtual Columnar Mapping: the
+ * sparse salient columns stored as a dense physical matrix, read through an
+ * index list; Sec. 4: the Kb-sS-gG configurations use the same K for both).
+ * After the K global bases, the residual at the S = s * (N/g) columns idx[p]
+ * (normally the s salient columns of group j at p = j*s .. j*s+s-1, chosen
+ * by the caller) is gathered into Rs [M][S] and fitted by the same grouped
+ * recipe with groups of s physical columns:
+ *   sbits     (device) out: K bases of M x S signs in the device layout with
+ *             ceil(S/32) words per row (bits at or beyond S clear)
+ *   salpha    (device) out: fp16 row scales, word-grouped: the 32/s scales of
+ *             one sign word of one row adjacent, (k, w, m, t) at
+ *             ((k * ceil(S/32) + w) * M + m) * (32/s) + t for group
+ *             j = w * (32/s) + t (slots past the last group are 0); 8-byte aligned
+ *   scolscale (device) out: fp16 [K][S] (with BSG_PACK_COLSCALE)
+ *   idx       (device) in: int32 [S], 16-byte aligned; an index outside
+ *             [0, N) reads a zero column
+ * s = 8, 16 or 32; s = 0 packs the global bases only.  workspace >=
+ * bsq_pack_hybrid_workspace_bytes (0 for invalid sizes).  Bit-exact as
+ * bsq_pack_grouped.
+ */
+BSG_API size_t bsq_pack_hybrid_workspace_bytes(int M, int N, int g, int s);
+BSG_API bsg_status bsq_pack_hybrid(const float* W, int M, int N, int K, int g, int s, const int32_t* idx, int flags,
+                                   uint32_t* bits, uint16_t* alpha, uint16_t* colscale, uint32_t* sbits,
+                                   uint16_t* salpha, uint16_t* scolscale, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * bs_gemv_grouped -- bs_gemv with group-wise row scales (FluxBin Sec. 3.1):
  *   y[m,b] (= or +=) sum_k sum_j alpha_k[m][j] *
  *                    sum_{n in group j} (2 bit_k(m,n) - 1) * c_k[n] * x[n,b]
- *   alpha     (device) fp32 [K][N/g][M], group-major as bsq_pack_grouped writes it
+ *   alpha     (device) fp16 [K][N/g][M], group-major as bsq_pack_grouped writes it
  *   other arguments as bs_gemv.
  * 1 <= K <= 4, g a power of two >= 64 dividing N, 1 <= B <= 64 (one launch
  * per batch column).  fp32 sums in a fixed order, within
  * 2e-3 * sum_k sum_j |alpha_k[m][j]| * sum_{n in j} |c_k[n] x[n,b]|.
  */
-BSG_API bsg_status bs_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, const float* alpha,
+BSG_API bsg_status bs_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, const uint16_t* alpha,
                                    const uint16_t* colscale, const void* x, int x_dtype, int B, float* y,
                                    int accumulate, void* stream);
+
+/*
+ * bs_gemv_hybrid -- bs_gemv_grouped plus the salient-column bases of
+ * bsq_pack_hybrid, in the same launch (FluxBin Sec. 3.2: the salient phase
+ * runs through the same kernel, its activations gathered by the index list):
+ *   y[m,b] += sum_k sum_j salpha_k[m][j] *
+ *             sum_{i < s} (2 sbit_k(m, j*s+i) - 1) * sc_k[j*s+i] * x[idx[j*s+i], b]
+ * Arguments as written by bsq_pack_hybrid; s = 8, 16 or 32 (0: no salient
+ * branch, as bs_gemv_grouped).  Column scales on both branches or on
+ * neither (BSG_ERR_SHAPE otherwise); scolscale 8-byte aligned.  Within the bs_gemv_grouped bound plus
+ * the same term for the salient branch.
+ */
+BSG_API bsg_status bs_gemv_hybrid(const uint32_t* bits, int K, int M, int N, int g, const uint16_t* alpha,
+                                  const uint16_t* colscale, const uint32_t* sbits, int s, const int32_t* idx,
+                                  const uint16_t* salpha, const uint16_t* scolscale, const void* x, int x_dtype,
+                                  int B, float* y, int accumulate, void* stream);
 
 /*
  * bs_gemv_multi -- several bs_gemv products that share x, in one launch

@@ -195,7 +195,7 @@ def test_grouped_validation():
     assert _gg(M=0) == OK
     assert _gg(bits=None) == ENULL
     assert _gg(alpha=None) == ENULL
-    assert _gg(alpha=A16b + 2) == EALIGN
+    assert _gg(alpha=A16b + 1) == EALIGN   # fp16 scales
     assert _gg(bits=A16 + 4) == EALIGN
     assert bsg.lib().bsq_pack_grouped_workspace_bytes(64, 256, 128) >= 64 * 256 * 8
     assert bsg.lib().bsq_pack_grouped_workspace_bytes(64, 256, 96) == 0
@@ -205,6 +205,39 @@ def test_grouped_validation():
     assert pg(A16, 64, 256, 2, 128, 1, A16b, A16c, None, A16d, nb, None) == ENULL   # colscale requested
     assert pg(A16, 64, 256, 2, 128, 0, A16b, A16c, None, A16d, nb - 1, None) == EWS
     assert pg(A16, 64, 256, 2, 128, 4, A16b, A16c, None, A16d, nb, None) == ESHAPE  # unknown flag
+
+
+def _gh(s=16, sbits=A16, idx=A16b, salpha=A16c, scs=None, cs=None, K=2, M=128, N=256, g=128, dt=2, B=1):
+    return bsg.lib().bs_gemv_hybrid(A16, K, M, N, g, A16b, cs, sbits, s, idx, salpha, scs, A16c, dt, B, A16d, 0,
+                                    None)
+
+
+@fake_ptrs
+def test_hybrid_validation():
+    assert _gh(s=12) == ESHAPE
+    assert _gh(s=4) == ESHAPE
+    assert _gh(s=64) == ESHAPE
+    assert _gh(K=5) == ESHAPE
+    assert _gh(cs=A16d) == ESHAPE              # column scales on one branch only
+    assert _gh(scs=A16d) == ESHAPE
+    assert _gh(sbits=None) == ENULL
+    assert _gh(idx=None) == ENULL
+    assert _gh(salpha=None) == ENULL
+    assert _gh(s=0, sbits=None, idx=None, salpha=None, M=0) == OK   # no salient branch: nothing needed
+    assert _gh(idx=A16b + 4) == EALIGN         # 16-byte index loads
+    assert _gh(salpha=A16c + 4) == EALIGN      # 8-byte scale loads
+    assert _gh(M=0) == OK
+    wb = bsg.lib().bsq_pack_hybrid_workspace_bytes
+    assert wb(64, 256, 128, 16) >= 64 * 256 * 8 + 64 * 32 * 8
+    assert wb(64, 256, 128, 12) == 0
+    assert wb(64, 256, 128, 0) == bsg.lib().bsq_pack_grouped_workspace_bytes(64, 256, 128)
+    nb = wb(64, 256, 128, 8)
+    ph = bsg.lib().bsq_pack_hybrid
+    assert ph(A16, 64, 256, 2, 128, 8, None, 0, A16b, A16c, None, A16d, A16c, None, A16d, nb, None) == ENULL
+    assert ph(A16, 64, 256, 2, 128, 8, A16b, 0, A16b, A16c, None, None, A16c, None, A16d, nb, None) == ENULL
+    assert ph(A16, 64, 256, 2, 128, 8, A16b, 1, A16b, A16c, A16d, A16d, A16c, None, A16d, nb, None) == ENULL
+    assert ph(A16, 64, 256, 2, 128, 8, A16b, 0, A16b, A16c, None, A16d, A16c, None, A16d, nb - 1, None) == EWS
+    assert ph(A16, 64, 256, 2, 128, 24, A16b, 0, A16b, A16c, None, A16d, A16c, None, A16d, nb, None) == ESHAPE
 
 
 @fake_ptrs
