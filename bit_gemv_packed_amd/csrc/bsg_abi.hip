@@ -203,7 +203,11 @@ bsg_status bs_gemv(const uint32_t* bits, int K, int M, int N, const float* alpha
   a.xdt = x_dtype;
   a.accumulate = accumulate ? 1 : 0;
   a.xvec = xvec_ok(x, colscale);
-  if (mfma_eligible(B, x_dtype, colscale != nullptr)) return hip_status(launch_prod_mfma(a, (hipStream_t)stream));
+  // matrix cores for B >= 4 columns of 16-bit x; with column scales for fp16
+  // x whose scales are 4-byte aligned (2 scales per load)
+  if (mfma_eligible(B, x_dtype, colscale != nullptr) ||
+      (colscale && !misaligned(colscale, 4) && mfma_cg_ok(B, x_dtype, x, true, 0, M)))
+    return hip_status(launch_prod_mfma(a, (hipStream_t)stream));
   return hip_status(launch_prod_f(a, p, (hipStream_t)stream));
 }
 
@@ -353,6 +357,11 @@ bsg_status bs_gemv_hybrid(const uint32_t* bits, int K, int M, int N, int g, cons
     a.vs_cs = scolscale;
     a.vs_gpw = 32 / s;
   }
+  // B >= 4 columns without salient columns: the matrix cores (g >= 128, M % 4 == 0, fp16 x with column
+  // scales, 4-byte aligned scales)
+  if (!s && !misaligned(alpha, 8) && !misaligned(colscale, 4) &&
+      mfma_cg_ok(B, x_dtype, x, colscale != nullptr, a.gsw, M))
+    return hip_status(launch_prod_mfma(a, (hipStream_t)stream));
   return hip_status(launch_prod_grouped(a, (hipStream_t)stream));
 }
 

@@ -147,6 +147,9 @@ bool mfma_eligible(int B, int xdt, bool colscale);
 hipError_t launch_prod_mfma(const ProdArgs& a, hipStream_t s);
 // The matrix-core path can fuse projections (a.np > 1) for this B and x.
 bool mfma_multi_ok(int B, const void* x);
+// The matrix-core path takes column scales (fp16 x) and group-wise row scales
+// (a.gsw words per group, >= 4) for this B, x and M.
+bool mfma_cg_ok(int B, int xdt, const void* x, bool colscale, int gsw, int M);
 hipError_t launch_prod_i8(const ProdArgs& a, const ProdPlan& p, hipStream_t s);
 
 }  // namespace bsg

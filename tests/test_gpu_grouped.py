@@ -334,3 +334,36 @@ def test_pack_then_gemv_hybrid_end_to_end():
     rb, ra, rc, rsb, rsa, rsc = oracle.pack_hybrid(W, K, g, s, idx, True)
     ref = oracle.sign_gemv_hybrid(rb, K, M, N, g, ra, rc, rsb, s, idx, rsa, rsc, x)
     check_close(y.cpu().numpy(), ref, _hybrid_tol(ra, rc, rsa, rsc, idx, x, g, s) + 1e-9, "pack -> gemv hybrid")
+
+
+# ------------------------------------------------------------------ batches on the matrix cores
+# B >= 4 columns of 16-bit x with g >= 128 and M % 4 == 0 (and fp16 x when
+# there are column scales) run on the matrix cores; the others per column on
+# the table kernel.  Both are held to the per-group bound; the matrix-core
+# cases also to a ten times tighter one (exact products, fp32 sums).
+GROUPED_BATCH_CASES = [
+    # M, N, K, g, B, colscale, dtype, matrix cores
+    (256, 512, 2, 128, 4, False, "bf16", True),
+    (132, 1024, 3, 256, 8, True, "f16", True),
+    (1000, 4096, 4, 128, 16, False, "bf16", True),
+    (4096, 4096, 2, 128, 16, True, "f16", True),
+    (300, 1024, 1, 512, 32, False, "f16", True),
+    (9000, 512, 2, 128, 20, True, "f16", True),     # 32-row tiles, two batch launches
+    (130, 1024, 2, 128, 16, True, "f16", False),    # M % 4 != 0
+    (200, 2048, 2, 64, 8, True, "f16", False),      # g = 64
+    (256, 1024, 2, 128, 8, True, "bf16", False),    # column scales with bf16 x
+]
+
+
+@pytest.mark.parametrize("case", GROUPED_BATCH_CASES, ids=lambda c: "M%d_N%d_K%d_g%d_B%d_cs%d_%s_mc%d" % c)
+def test_gemv_grouped_batches(case):
+    M, N, K, g, B, cs, dt, mc = case
+    say("bs_gemv_grouped batch", case)
+    L, alpha, csb, x = _inputs(M, N, K, g, B, cs, dt, M + N + K + g + B + 7)
+    bits = bsg.bsg_logical_to_layout(to_dev(L.view(np.int32)), K, M, N)
+    y = bsg.bs_gemv_grouped(bits, K, M, N, g, f16_dev(_gm(alpha)), x_dev(x, dt),
+                            colscale=f16_dev(csb) if cs else None)
+    torch.cuda.synchronize()
+    ref = oracle.sign_gemv_grouped(L, K, M, N, g, alpha, x, csb)
+    check_close(y.cpu().numpy(), ref, _bound(alpha, csb, x, g, 2e-4 if mc else 2e-3) + 1e-9,
+                "grouped batch %s" % (case,))

@@ -132,3 +132,64 @@ def test_mfma_agrees_with_table_path_on_integer_x():
     for b in range(B):
         check_close(cols[b][:, 0].cpu().numpy(), y[:, b].cpu().numpy().astype(np.float64), tol[:, b],
                     "table vs mfma, column %d" % b)
+
+
+# ------------------------------------------------------------------ column scales (fp16 x)
+# The A values are the column scales' own fp16 bits with the sign flipped for
+# a set weight bit, so products with fp16 x stay exact and the same 2e-4 bound
+# holds (sum_n |c_k[n] x[n,b]| in place of sum_n |x[n,b]|).
+CS_CASES = [
+    # K, M, N, B, negative scales too
+    (1, 16, 32, 4, False),
+    (2, 64, 128, 8, False),
+    (2, 100, 4096, 16, False),
+    (3, 257, 544, 4, True),
+    (4, 130, 1056, 20, False),
+    (6, 300, 2080, 32, True),     # two launches of bases
+    (2, 9000, 256, 16, False),    # 32-row tiles
+    (8, 65, 256, 8, True),
+    (2, 200, 512, 6, False),      # B % 4 != 0: the table path
+]
+
+
+@pytest.mark.parametrize("case", CS_CASES, ids=lambda c: "K%d_M%d_N%d_B%d_neg%d" % c)
+def test_mfma_colscale_matches_oracle(case):
+    K, M, N, B, neg = case
+    say("mfma bs_gemv colscale", case)
+    seed = 60000 + K * 7919 + M * 31 + N + B
+    L = synth.random_bits(seed, K, M, N)
+    alpha, cs = synth.random_scales(seed, K, M, N, True)
+    if neg:
+        r = np.random.default_rng([61, seed])
+        cs = (cs.view(np.float16) * np.where(r.integers(0, 2, cs.shape) == 1, 1, -1).astype(np.float16)).view(np.uint16)
+    x = synth.random_x(seed, N, B, "f16", "normal")
+    bits = _layout(L, K, M, N)
+    csd = torch.from_numpy(np.ascontiguousarray(cs).view(np.int16)).to(DEV)
+    y = bsg.bs_gemv(bits, K, M, N, to_dev(alpha), x_dev(x, "f16"), colscale=csd)
+    torch.cuda.synchronize()
+    ref = oracle.sign_gemv(L, K, M, N, alpha, x, cs)
+    rel = MFMA_REL if B % 4 == 0 else 2e-3
+    tol = oracle.tolerance(x, alpha=alpha, colscale_f16=cs, rel=rel)
+    check_close(y.cpu().numpy(), ref, tol + 1e-9, "mfma colscale %s" % (case,))
+
+
+def test_mfma_colscale_equals_the_table_path_on_small_integers():
+    """Small-integer x and power-of-two column scales: every partial sum is
+    exact on both paths, so the batched product equals the per-column (table)
+    products up to the final row-scale rounding."""
+    K, M, N, B = 2, 200, 1024, 8
+    say("mfma colscale vs table", K, M, N, B)
+    L = synth.random_bits(71, K, M, N)
+    alpha, _ = synth.random_scales(71, K, M, N, False)
+    r = np.random.default_rng(71)
+    cs = (2.0 ** r.integers(-2, 3, size=(K, N))).astype(np.float16).view(np.uint16)
+    x = r.integers(-8, 9, size=(N, B)).astype(np.float32)
+    bits = _layout(L, K, M, N)
+    csd = torch.from_numpy(cs.view(np.int16)).to(DEV)
+    ad = to_dev(alpha)
+    y = bsg.bs_gemv(bits, K, M, N, ad, x_dev(x, "f16"), colscale=csd)
+    cols = [bsg.bs_gemv(bits, K, M, N, ad, x_dev(np.ascontiguousarray(x[:, b]), "f16"), colscale=csd)
+            for b in range(B)]
+    torch.cuda.synchronize()
+    yt = torch.cat(cols, dim=1).cpu().numpy()
+    np.testing.assert_allclose(y.cpu().numpy(), yt, rtol=1e-6, atol=1e-6)
