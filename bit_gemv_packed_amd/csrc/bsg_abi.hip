@@ -357,11 +357,18 @@ bsg_status bs_gemv_hybrid(const uint32_t* bits, int K, int M, int N, int g, cons
     a.vs_cs = scolscale;
     a.vs_gpw = 32 / s;
   }
-  // B >= 4 columns without salient columns: the matrix cores (g >= 128, M % 4 == 0, fp16 x with column
-  // scales, 4-byte aligned scales)
-  if (!s && !misaligned(alpha, 8) && !misaligned(colscale, 4) &&
-      mfma_cg_ok(B, x_dtype, x, colscale != nullptr, a.gsw, M))
-    return hip_status(launch_prod_mfma(a, (hipStream_t)stream));
+  // B >= 4 columns on the matrix cores (g >= 128, M % 4 == 0, fp16 x with column scales, 4-byte
+  // aligned scales); the salient columns then with fp16 x, in a second launch that adds onto y
+  const bool mc = !misaligned(alpha, 8) && !misaligned(colscale, 4) &&
+                  mfma_cg_ok(B, x_dtype, x, colscale != nullptr, a.gsw, M);
+  if (mc && !s) return hip_status(launch_prod_mfma(a, (hipStream_t)stream));
+  if (mc && vcm_mfma_ok(B, x_dtype, x, K, a.vs_S, scolscale != nullptr)) {
+    ProdArgs am = a;
+    am.vs_bits = nullptr;
+    const hipError_t e = launch_prod_mfma(am, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(launch_vcm_mfma(a, (hipStream_t)stream));
+  }
   return hip_status(launch_prod_grouped(a, (hipStream_t)stream));
 }
 

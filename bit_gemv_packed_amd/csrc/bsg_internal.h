@@ -150,6 +150,10 @@ bool mfma_multi_ok(int B, const void* x);
 // The matrix-core path takes column scales (fp16 x) and group-wise row scales
 // (a.gsw words per group, >= 4) for this B, x and M.
 bool mfma_cg_ok(int B, int xdt, const void* x, bool colscale, int gsw, int M);
+// Salient-column bases (a.vs_*) on the matrix cores after the main product
+// (bsg_vcm_mfma.hip): fp16 x, B >= 4, K <= 4, the gathered x within the LDS.
+bool vcm_mfma_ok(int B, int xdt, const void* x, int K, int S, bool cs);
+hipError_t launch_vcm_mfma(const ProdArgs& a, hipStream_t s);
 hipError_t launch_prod_i8(const ProdArgs& a, const ProdPlan& p, hipStream_t s);
 
 }  // namespace bsg

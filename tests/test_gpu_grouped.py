@@ -367,3 +367,47 @@ def test_gemv_grouped_batches(case):
     ref = oracle.sign_gemv_grouped(L, K, M, N, g, alpha, x, csb)
     check_close(y.cpu().numpy(), ref, _bound(alpha, csb, x, g, 2e-4 if mc else 2e-3) + 1e-9,
                 "grouped batch %s" % (case,))
+
+
+# B >= 4 columns of fp16 x: the main bases on the matrix cores, then the salient
+# bases in a second matrix-core launch (gathered x in LDS, the group scale
+# folded into the A values); bf16 x or M % 4 != 0: per column on the table
+# kernel.  All within the per-group bound.
+HYBRID_BATCH_CASES = [
+    # M, N, K, g, s, B, colscale, dtype
+    (256, 512, 2, 128, 16, 4, True, "f16"),
+    (132, 1152, 2, 128, 8, 8, True, "f16"),       # S = 72: a partial tile and word
+    (1000, 4096, 3, 128, 16, 16, False, "f16"),
+    (4096, 4096, 2, 128, 8, 16, True, "f16"),
+    (300, 1024, 4, 256, 32, 20, True, "f16"),     # two batch launches
+    (9000, 512, 2, 128, 16, 16, True, "f16"),     # 32-row tiles
+    (256, 512, 2, 128, 16, 4, True, "bf16"),      # table path
+    (130, 1024, 2, 128, 8, 8, True, "f16"),       # M % 4 != 0: table path
+]
+
+
+@pytest.mark.parametrize("case", HYBRID_BATCH_CASES, ids=lambda c: "M%d_N%d_K%d_g%d_s%d_B%d_cs%d_%s" % c)
+def test_gemv_hybrid_batches(case):
+    M, N, K, g, s, B, cs, dt = case
+    say("bs_gemv_hybrid batch", case)
+    L, alpha, csb, SL, salpha, scs, idx, x = _hybrid_inputs(M, N, K, g, s, B, cs, dt, M + N + K + g + s + B + 11)
+    y = _hybrid_run(M, N, K, g, s, cs, dt, L, alpha, csb, SL, salpha, scs, idx, x)
+    torch.cuda.synchronize()
+    ref = oracle.sign_gemv_hybrid(L, K, M, N, g, alpha, csb, SL, s, idx, salpha, scs, x)
+    check_close(y.cpu().numpy(), ref, _hybrid_tol(alpha, csb, salpha, scs, idx, x, g, s) + 1e-9,
+                "hybrid batch %s" % (case,))
+
+
+def test_gemv_hybrid_batch_index_outside_the_matrix_reads_zero():
+    M, N, K, g, s, B = 256, 512, 2, 128, 16, 8
+    say("bs_gemv_hybrid batch bad index", M, N, K, g, s, B)
+    L, alpha, csb, SL, salpha, scs, idx, x = _hybrid_inputs(M, N, K, g, s, B, True, "f16", 47)
+    bad = [0, 31, 63]
+    idx_bad = idx.copy()
+    idx_bad[bad] = [N, -7, 1 << 29]
+    y = _hybrid_run(M, N, K, g, s, True, "f16", L, alpha, csb, SL, salpha, scs, idx_bad, x)
+    torch.cuda.synchronize()
+    scs0 = scs.copy()
+    scs0[:, bad] = 0
+    ref = oracle.sign_gemv_hybrid(L, K, M, N, g, alpha, csb, SL, s, idx, salpha, scs0, x)
+    check_close(y.cpu().numpy(), ref, _hybrid_tol(alpha, csb, salpha, scs, idx, x, g, s) + 1e-9, "batch bad index")
