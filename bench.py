@@ -275,46 +275,48 @@ def run_rows(steps, warmup):
         torch.cuda.empty_cache()
 
     # f3: group-wise fp16 row scales (FluxBin Kb-g128) and the salient columns read through the
-    # Virtual Columnar Mapping (Kb-sS-g128), on LLaMA-2-7B projection shapes
+    # Virtual Columnar Mapping (Kb-sS-g128), on LLaMA-2-7B projection shapes, fp16 x (FluxBin's
+    # models run in fp16); batch 16 on the matrix cores
     for name, M, N in [("q/o 4096x4096", 4096, 4096), ("gate/up 11008x4096", 11008, 4096),
                        ("down 4096x11008", 4096, 11008)]:
         K, g = 2, 128
         G = N // g
-        for s in (0, 8, 16):
-            S = s * G
-            nds = (S + 31) // 32
-            gpw = 32 // s if s else 1
-            wb = K * M * N // 8 + 2 * K * M * G + 2 * K * N
-            if s:
-                wb += 4 * K * M * nds + 2 * K * nds * M * gpw + 2 * K * S + 4 * S
-            n = copies(wb)
-            bits = rand_bits(K, M, N, n)
-            al = (torch.rand((n, K, G, M), device=dev) * 0.02).half().view(torch.int16)
-            csd = (torch.rand((n, K, N), device=dev) + 0.5).half().view(torch.int16)
-            x = xs(N, 1, n)
-            y = torch.empty((n, M, 1), device=dev)
-            if s:
-                sb = rand_bits(K, M, nds * 32, n)
-                sa = (torch.rand((n,) + bsg.salient_scale_shape(K, M, N, g, s), device=dev) * 0.01).half() \
-                    .view(torch.int16)
-                sc = (torch.rand((n, K, S), device=dev) + 0.5).half().view(torch.int16)
-                # s distinct columns of every group of g per copy (seeded, drawn on the host)
-                keys = np.random.default_rng([7, M, N, s]).random((n, G, g))
-                pick = np.sort(np.argsort(keys, axis=2)[:, :, :s], axis=2) + (np.arange(G) * g)[None, :, None]
-                idx = torch.from_numpy(pick.reshape(n, S).astype(np.int32)).to(dev)
-                step = lambda i: bsg.bs_gemv_hybrid(bits[i % n], K, M, N, g, al[i % n], x[i % n], colscale=csd[i % n],
-                                                    sbits=sb[i % n], s=s, idx=idx[i % n], salpha=sa[i % n],
-                                                    scolscale=sc[i % n], y=y[i % n])
-                op = "bs_gemv_hybrid (2b-s%d-g128, 1 launch)" % s
-            else:
-                step = lambda i: bsg.bs_gemv_grouped(bits[i % n], K, M, N, g, al[i % n], x[i % n],
-                                                     colscale=csd[i % n], y=y[i % n])
-                op = "bs_gemv_grouped (2b-g128)"
-            emit("f3", op, name, _graph_us(step, steps, warmup), wb + 2 * N, K=K, g=g, s=s)
-            del bits, al, csd, x, y
-            if s:
-                del sb, sa, sc, idx
-            torch.cuda.empty_cache()
+        for B in (1, 16):
+            for s in (0, 8, 16):
+                S = s * G
+                nds = (S + 31) // 32
+                gpw = 32 // s if s else 1
+                wb = K * M * N // 8 + 2 * K * M * G + 2 * K * N
+                if s:
+                    wb += 4 * K * M * nds + 2 * K * nds * M * gpw + 2 * K * S + 4 * S
+                n = copies(wb)
+                bits = rand_bits(K, M, N, n)
+                al = (torch.rand((n, K, G, M), device=dev) * 0.02).half().view(torch.int16)
+                csd = (torch.rand((n, K, N), device=dev) + 0.5).half().view(torch.int16)
+                x = xs(N, B, n, torch.float16)
+                y = torch.empty((n, M, B), device=dev)
+                if s:
+                    sb = rand_bits(K, M, nds * 32, n)
+                    sa = (torch.rand((n,) + bsg.salient_scale_shape(K, M, N, g, s), device=dev) * 0.01).half() \
+                        .view(torch.int16)
+                    sc = (torch.rand((n, K, S), device=dev) + 0.5).half().view(torch.int16)
+                    # s distinct columns of every group of g per copy (seeded, drawn on the host)
+                    keys = np.random.default_rng([7, M, N, s]).random((n, G, g))
+                    pick = np.sort(np.argsort(keys, axis=2)[:, :, :s], axis=2) + (np.arange(G) * g)[None, :, None]
+                    idx = torch.from_numpy(pick.reshape(n, S).astype(np.int32)).to(dev)
+                    step = lambda i: bsg.bs_gemv_hybrid(bits[i % n], K, M, N, g, al[i % n], x[i % n],
+                                                        colscale=csd[i % n], sbits=sb[i % n], s=s, idx=idx[i % n],
+                                                        salpha=sa[i % n], scolscale=sc[i % n], y=y[i % n])
+                    op = "bs_gemv_hybrid (2b-s%d-g128, %s)" % (s, "1 launch" if B == 1 else "2 launches, matrix cores")
+                else:
+                    step = lambda i: bsg.bs_gemv_grouped(bits[i % n], K, M, N, g, al[i % n], x[i % n],
+                                                         colscale=csd[i % n], y=y[i % n])
+                    op = "bs_gemv_grouped (2b-g128%s)" % ("" if B == 1 else ", matrix cores")
+                emit("f3", op, name, _graph_us(step, steps, warmup), wb + 2 * N * B, K=K, B=B, g=g, s=s)
+                del bits, al, csd, x, y
+                if s:
+                    del sb, sa, sc, idx
+                torch.cuda.empty_cache()
 
     # a4, a5: the fused layer (bases + binary low-rank + protected int8 rows) and its parts
     for name, M, N, K, r, frac in [("5120x5120 K=3 r=512", 5120, 5120, 3, 512, 0.0),
