@@ -1,6 +1,8 @@
 // Offline packing on gfx950: greedy residual binary bases (FluxBin Sec. 2,
-// Sec. 3.1), sign packing of the low-rank factors (BiLoCo "The core idea"),
-// and the protected int8 rows (BiSCo "Sensitivity Protection").
+// Sec. 3.1), with per-row or group-wise fp16 row scales and the salient-
+// column bases of its hybrid format (Sec. 3.1, 3.2), sign packing of the
+// low-rank factors (BiLoCo "The core idea"), and the protected int8 rows
+// (BiSCo "Sensitivity Protection").
 //
 // Every floating-point sum here runs in fp64 in ascending index order, with
 // FMA contraction off, so the packed bits and scales are bit-exact with a
