@@ -48,9 +48,10 @@ hipError_t launch_prod_grouped(const ProdArgs& a0, hipStream_t st) {
   const int wmax = prod_max_waves(p.KM, p.BB, a0.vs_bits ? 2 : 1, p.XM);
   if (p.W > wmax) {
     const int T = (a0.ND + p.CW - 1) / p.CW;
-    p.lds = p.lds / p.W * wmax;
-    p.W = wmax;
-    p.NCH = (T + p.W - 1) / p.W;
+    const size_t per_wave = p.lds / p.W;
+    p.NCH = (T + wmax - 1) / wmax;
+    p.W = (T + p.NCH - 1) / p.NCH;  // no wavefront without chunks
+    p.lds = per_wave * p.W;
   }
   for (int c = 0; c < p.nlaunch; ++c) {
     ProdArgs a = as;
