@@ -318,6 +318,35 @@ def run_rows(steps, warmup):
                     del sb, sa, sc, idx
                 torch.cuda.empty_cache()
 
+    # f2 x f3: the query, key and value projections in the 2b-g128 format in one launch, B = 1
+    K, g, N = 2, 128, 4096
+    G = N // g
+    qkv = [("q", 4096), ("k", 1024), ("v", 1024)]
+    wbs = {nm: K * M * N // 8 + 2 * K * M * G + 2 * K * N for nm, M in qkv}
+    n = copies(sum(wbs.values()))
+    P = {nm: (rand_bits(K, M, N, n), (torch.rand((n, K, G, M), device=dev) * 0.02).half().view(torch.int16),
+              (torch.rand((n, K, N), device=dev) + 0.5).half().view(torch.int16), torch.empty((n, M, 1), device=dev))
+         for nm, M in qkv}
+    x = xs(N, 1, n, torch.float16)
+    Mof = dict(qkv)
+
+    def gm_fused(i):
+        c = i % n
+        bsg.bs_gemv_grouped_multi([(P[nm][0][c], Mof[nm], P[nm][1][c], P[nm][2][c], P[nm][3][c]) for nm, _ in qkv],
+                                  K, N, g, x[c])
+
+    def gm_single(i):
+        c = i % n
+        for nm, M in qkv:
+            bsg.bs_gemv_grouped(P[nm][0][c], K, M, N, g, P[nm][1][c], x[c], colscale=P[nm][2][c], y=P[nm][3][c])
+    by = sum(wbs.values()) + 2 * N
+    emit("f3", "bs_gemv_grouped_multi (2b-g128, 1 launch)", "q+k+v 6144x4096", _graph_us(gm_fused, steps, warmup), by,
+         K=K, B=1, g=g)
+    emit("f3", "bs_gemv_grouped, one call per projection", "q+k+v 6144x4096", _graph_us(gm_single, steps, warmup), by,
+         K=K, B=1, g=g)
+    del P, x
+    torch.cuda.empty_cache()
+
     # a4, a5: the fused layer (bases + binary low-rank + protected int8 rows) and its parts
     for name, M, N, K, r, frac in [("5120x5120 K=3 r=512", 5120, 5120, 3, 512, 0.0),
                                    ("13824x5120 r=512 1% rows", 13824, 5120, 2, 512, 0.01),

@@ -61,6 +61,7 @@ _SIGS = {
     "bs_gemv_grouped": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P]),
     "bsq_pack_hybrid_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "bsq_pack_hybrid": (ctypes.c_int32, [_P, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "bs_gemv_grouped_multi": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _I, _I, _I, _P]),
     "bs_gemv_hybrid": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P]),
     "binlr_fit_workspace_bytes": (_SZ, [_I, _I, _I]),
     "binlr_fit": (ctypes.c_int32, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -352,7 +353,7 @@ def bs_gemv(bits, K: int, M: int, N: int, alpha, x, colscale=None, y=None, accum
 
 
 class BsgProj(ctypes.Structure):
-    """Mirror of bsg_proj (include/bsg.h)."""
+    """Mirror of bsg_proj and bsg_proj_grouped (include/bsg.h): the same field layout."""
     _fields_ = [("bits", ctypes.c_void_p), ("alpha", ctypes.c_void_p), ("colscale", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("M", ctypes.c_int)]
 
@@ -372,6 +373,25 @@ def bs_gemv_multi(projs, K: int, N: int, x, accumulate: bool = False):
         arr[i] = BsgProj(_ptr(bits), _ptr(alpha), _ptr(cs), _ptr(y), M)
     _check("bs_gemv_multi", lib().bs_gemv_multi(ctypes.cast(arr, ctypes.c_void_p), len(projs), K, N, _ptr(x),
                                                 _dtype_code(x), B, 1 if accumulate else 0, _stream(dev)))
+    return ys
+
+
+def bs_gemv_grouped_multi(projs, K: int, N: int, g: int, x, accumulate: bool = False):
+    """Several bs_gemv_grouped products sharing x, in one launch at B = 1.  projs: list of (bits, M,
+    alpha fp16 [K][N/g][M], colscale or None, y or None); returns the list of y (fp32 [M][B])."""
+    torch = _torch()
+    B = _xshape(x, N)
+    dev = x.device
+    arr = (BsgProj * max(1, len(projs)))()
+    ys = []
+    for i, (bits, M, alpha, cs, y) in enumerate(projs):
+        if y is None:
+            y = torch.empty((M, B), dtype=torch.float32, device=dev)
+        ys.append(y)
+        arr[i] = BsgProj(_ptr(bits), _ptr(alpha), _ptr(cs), _ptr(y), M)
+    _check("bs_gemv_grouped_multi", lib().bs_gemv_grouped_multi(ctypes.cast(arr, ctypes.c_void_p), len(projs), K, N,
+                                                                g, _ptr(x), _dtype_code(x), B,
+                                                                1 if accumulate else 0, _stream(dev)))
     return ys
 
 

@@ -379,6 +379,67 @@ bsg_status bs_gemv_grouped(const uint32_t* bits, int K, int M, int N, int g, con
                         accumulate, stream);
 }
 
+bsg_status bs_gemv_grouped_multi(const bsg_proj_grouped* projs, int P, int K, int N, int g, const void* x,
+                                 int x_dtype, int B, int accumulate, void* stream) {
+  if (bad_dtype(x_dtype)) return BSG_ERR_DTYPE;
+  if (!projs) return BSG_ERR_NULL;
+  if (P < 1 || P > kMaxProj || K < 1 || K > 4 || bad_n(N) || bad_group(N, g) || B < 1 || B > kMaxB)
+    return BSG_ERR_SHAPE;
+  const bool cs = projs[0].colscale != nullptr;
+  for (int i = 0; i < P; ++i) {
+    const bsg_proj_grouped& d = projs[i];
+    if (d.M < 0 || too_big(K, d.M, N, B) || (size_t)K * d.M * (N / g) >= (1u << 30) ||
+        (d.colscale != nullptr) != cs)
+      return BSG_ERR_SHAPE;
+  }
+  if (!x) return BSG_ERR_NULL;
+  if (misaligned(x, dtype_size(x_dtype))) return BSG_ERR_ALIGN;
+  int np = 0;
+  for (int i = 0; i < P; ++i) {
+    const bsg_proj_grouped& d = projs[i];
+    if (d.M == 0) continue;
+    if (!d.bits || !d.alpha || !d.y) return BSG_ERR_NULL;
+    if (misaligned(d.bits, 16) || misaligned(d.alpha, 2) || misaligned(d.colscale, 2) || misaligned(d.y, 4))
+      return BSG_ERR_ALIGN;
+    ++np;
+  }
+  if (np == 0) return BSG_OK;
+  if (np == 1 || B != 1) {
+    // one projection, or several batch columns: a product each
+    for (int i = 0; i < P; ++i) {
+      const bsg_proj_grouped& d = projs[i];
+      if (d.M == 0) continue;
+      const bsg_status r = bs_gemv_grouped(d.bits, K, d.M, N, g, d.alpha, d.colscale, x, x_dtype, B, d.y,
+                                           accumulate, stream);
+      if (r != BSG_OK) return r;
+    }
+    return BSG_OK;
+  }
+  ProdArgs a{};
+  a.x = x;
+  a.K = K;
+  a.N = N;
+  a.ND = N / 32;
+  a.B = B;
+  a.xdt = x_dtype;
+  a.accumulate = accumulate ? 1 : 0;
+  a.xvec = (((uintptr_t)x) % 16) == 0;
+  a.gsw = g / 32;
+  a.ngrp = N / g;
+  for (int i = 0; i < P; ++i) {
+    const bsg_proj_grouped& d = projs[i];
+    if (d.M == 0) continue;
+    ProjDesc& e = a.proj[a.np++];
+    e.bits = d.bits;
+    e.alpha = (const float*)(const void*)d.alpha;  // fp16 group scales, read as such
+    e.colscale = d.colscale;
+    e.y = d.y;
+    e.M = d.M;
+    if ((((uintptr_t)d.colscale) % 8) != 0) a.xvec = 0;
+  }
+  return hip_status(launch_prod_grouped(a, (hipStream_t)stream));
+}
+
 size_t binlr_fit_workspace_bytes(int M, int N, int r) {
   if (M < 1 || bad_n(N) || r < 1 || r > kMaxFitRank) return 0;
   return fit_workspace_bytes(M, N, r);

@@ -22,9 +22,19 @@ namespace bsg {
   BSG_PROD_XM(X, 2, 4, 3) BSG_PROD_XM(X, 2, 4, 4) BSG_PROD_XM(X, 4, 1, 3) BSG_PROD_XM(X, 4, 1, 4)            \
   BSG_PROD_XM(X, 2, 2, 3) BSG_PROD_XM(X, 2, 2, 4) BSG_PROD_XM(X, 1, 4, 3) BSG_PROD_XM(X, 1, 4, 4)
 
-// GS = 2: with the salient-column bases
+// GS = 2: with the salient-column bases; np > 1: fused projections (MP = 1)
 static hipError_t dispatch_gs(const ProdArgs& a, const ProdPlan& p, hipStream_t st) {
   const bool sal = a.vs_bits != nullptr;
+  if (a.np > 1) {
+    if (sal) return hipErrorInvalidConfiguration;
+    switch (prod_key(p.Q, p.NWL, p.KM, p.BB, p.XM)) {
+#define BSG_CASE(Q, NWL, KM, BB, XM) \
+  case prod_key(Q, NWL, KM, BB, XM): return launch_one(k_prod_f<Q, NWL, KM, BB, XM, 1, 1>, p, a, st);
+      BSG_PROD_GS_INSTANCES(BSG_CASE)
+#undef BSG_CASE
+      default: return hipErrorInvalidConfiguration;
+    }
+  }
   switch (prod_key(p.Q, p.NWL, p.KM, p.BB, p.XM)) {
 #define BSG_CASE(Q, NWL, KM, BB, XM)                                                           \
   case prod_key(Q, NWL, KM, BB, XM):                                                           \
@@ -37,12 +47,40 @@ static hipError_t dispatch_gs(const ProdArgs& a, const ProdPlan& p, hipStream_t 
 }
 
 hipError_t launch_prod_grouped(const ProdArgs& a0, hipStream_t st) {
-  ProdPlan p = plan_prod(a0.K, a0.M, a0.N, a0.B, a0.colscale != nullptr, false, a0.gsw);
-  if (p.KM > 4 || p.BB != 1) return hipErrorInvalidConfiguration;
+  const bool multi = a0.np > 1;
+  int mt = a0.M;
+  if (multi) {
+    mt = 0;
+    for (int i = 0; i < a0.np; ++i) mt += a0.proj[i].M;
+  }
+  // the tables per wavefront depend on the column scales (one set per base)
+  const bool cs = multi ? a0.proj[0].colscale != nullptr : a0.colscale != nullptr;
+  ProdPlan p = plan_prod(a0.K, mt, a0.N, a0.B, cs, false, a0.gsw);
+  if (p.KM > 4 || p.BB != 1 || (multi && a0.B != 1)) return hipErrorInvalidConfiguration;
   ProdArgs as = a0;
+  if (multi) {
+    // every projection's row blocks in one grid; the kernel prologue reads
+    // the first projection's operands before it switches to its own
+    int wg = 0;
+    for (int i = 0; i < as.np; ++i) {
+      ProjDesc& d = as.proj[i];
+      d.plane = plane_words(d.M, as.ND);
+      d.wg0 = wg;
+      d.al_bytes = (uint32_t)((size_t)as.K * as.ngrp * d.M * 2);
+      d.cs_bytes = d.colscale ? (uint32_t)((size_t)as.K * as.N * 2) : 0u;
+      wg += (d.M + p.RW - 1) / p.RW;
+    }
+    p.nwg = wg;
+    as.bits = as.proj[0].bits;
+    as.alpha = as.proj[0].alpha;
+    as.colscale = as.proj[0].colscale;
+    as.y = as.proj[0].y;
+    as.plane = as.proj[0].plane;
+    as.M = as.proj[0].M;
+  }
   as.x_bytes = (uint32_t)((size_t)a0.N * a0.B * (a0.xdt == BSG_F32 ? 4 : 2));
-  as.cs_bytes = a0.colscale ? (uint32_t)((size_t)a0.K * a0.N * 2) : 0u;
-  as.al_bytes = (uint32_t)((size_t)a0.K * a0.M * a0.ngrp * 2);
+  as.cs_bytes = as.colscale ? (uint32_t)((size_t)a0.K * a0.N * 2) : 0u;
+  as.al_bytes = (uint32_t)((size_t)as.K * as.M * as.ngrp * 2);
   p.XM = (a0.B == 1 && a0.xvec && a0.xdt != BSG_F32) ? (a0.xdt == BSG_BF16 ? 1 : 2) : 0;
   // the instance for this XM may allow fewer wavefronts than the plan took
   const int wmax = prod_max_waves(p.KM, p.BB, a0.vs_bits ? 2 : 1, p.XM);

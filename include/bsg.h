@@ -299,6 +299,26 @@ BSG_API bsg_status bs_gemv_hybrid(const uint32_t* bits, int K, int M, int N, int
                                   int B, float* y, int accumulate, void* stream);
 
 /*
+ * bs_gemv_grouped_multi -- several bs_gemv_grouped products that share x
+ * (e.g. the query, key and value projections in FluxBin's Kb-gG format), in
+ * one launch at B = 1 (each workgroup looks up its projection's rows); for
+ * B > 1 or one projection, a bs_gemv_grouped call each.
+ *   projs[p].alpha: fp16 [K][N/g][projs[p].M], group-major, as bs_gemv_grouped
+ * 1 <= P <= 8, 1 <= K <= 4, g as bs_gemv_grouped; column scales on every
+ * projection or on none (BSG_ERR_SHAPE otherwise); M = 0 projections are
+ * skipped.  Errors and bound as bs_gemv_grouped.
+ */
+typedef struct bsg_proj_grouped {
+  const uint32_t* bits;
+  const uint16_t* alpha;
+  const uint16_t* colscale;
+  float* y;
+  int M;
+} bsg_proj_grouped;
+BSG_API bsg_status bs_gemv_grouped_multi(const bsg_proj_grouped* projs, int P, int K, int N, int g, const void* x,
+                                         int x_dtype, int B, int accumulate, void* stream);
+
+/*
  * bs_gemv_multi -- several bs_gemv products that share x, in one launch
  * (projections that read the same activations, e.g. the query, key and
  * value projections, or the two projections of a gated MLP):

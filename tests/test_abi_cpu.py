@@ -313,3 +313,32 @@ def test_pack_validation():
     assert L.bsq_salient(A16, 64, 64, A16b, 65, A16c, A16d, A16, A16b, 1, A16c, 1 << 20, None) == ESHAPE
     assert L.bsq_quantize_i8(A16, 5, 64, 1, A16b, A16c, None) == EDTYPE
     assert L.bsg_logical_to_layout(A16, 1, 64, 40, A16b, None) == ESHAPE
+
+
+@fake_ptrs
+def test_grouped_multi_validation():
+    import ctypes
+    P = bsg.BsgProj * 3
+    good = lambda: P(bsg.BsgProj(A16, A16b, None, A16d, 64), bsg.BsgProj(A16, A16b, None, A16d, 32),
+                     bsg.BsgProj(A16, A16b, None, A16d, 0))
+    gm = bsg.lib().bs_gemv_grouped_multi
+    arr = good()
+    ptr = ctypes.cast(arr, ctypes.c_void_p)
+    assert gm(ptr, 0, 2, 256, 128, A16c, 2, 1, 0, None) == ESHAPE
+    assert gm(ptr, 9, 2, 256, 128, A16c, 2, 1, 0, None) == ESHAPE
+    assert gm(ptr, 3, 5, 256, 128, A16c, 2, 1, 0, None) == ESHAPE      # K > 4
+    assert gm(ptr, 3, 2, 256, 96, A16c, 2, 1, 0, None) == ESHAPE       # bad group
+    assert gm(ptr, 3, 2, 256, 128, A16c, 7, 1, 0, None) == EDTYPE
+    assert gm(None, 3, 2, 256, 128, A16c, 2, 1, 0, None) == ENULL
+    assert gm(ptr, 3, 2, 256, 128, None, 2, 1, 0, None) == ENULL
+    arr[1].colscale = A16d
+    assert gm(ptr, 3, 2, 256, 128, A16c, 2, 1, 0, None) == ESHAPE      # column scales on one projection only
+    arr = good()
+    arr[0].alpha = A16b + 1
+    assert gm(ctypes.cast(arr, ctypes.c_void_p), 3, 2, 256, 128, A16c, 2, 1, 0, None) == EALIGN
+    arr = good()
+    arr[1].bits = None
+    assert gm(ctypes.cast(arr, ctypes.c_void_p), 3, 2, 256, 128, A16c, 2, 1, 0, None) == ENULL
+    zero = P(bsg.BsgProj(A16, A16b, None, A16d, 0), bsg.BsgProj(A16, A16b, None, A16d, 0),
+             bsg.BsgProj(None, None, None, None, 0))
+    assert gm(ctypes.cast(zero, ctypes.c_void_p), 3, 2, 256, 128, A16c, 2, 1, 0, None) == OK

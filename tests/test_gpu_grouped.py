@@ -411,3 +411,56 @@ def test_gemv_hybrid_batch_index_outside_the_matrix_reads_zero():
     scs0[:, bad] = 0
     ref = oracle.sign_gemv_hybrid(L, K, M, N, g, alpha, csb, SL, s, idx, salpha, scs0, x)
     check_close(y.cpu().numpy(), ref, _hybrid_tol(alpha, csb, salpha, scs, idx, x, g, s) + 1e-9, "batch bad index")
+
+
+# ------------------------------------------------------------------ fused projections
+GROUPED_MULTI_CASES = [
+    # heights, N, K, g, B, colscale, dtype
+    ((256, 64, 64), 1024, 2, 128, 1, True, "f16"),            # q, k, v
+    ((130, 0, 33, 200), 512, 1, 64, 1, False, "bf16"),        # ragged, an empty projection
+    ((64,) * 8, 768, 3, 256, 1, True, "bf16"),                # eight projections
+    ((300, 100), 1088, 4, 64, 1, True, "f32"),                # partial last chunk
+    ((256, 128), 1024, 2, 128, 3, True, "bf16"),              # B > 1: a call each
+    ((256, 128), 1024, 2, 128, 16, True, "f16"),              # B = 16: matrix cores each
+]
+
+
+@pytest.mark.parametrize("case", GROUPED_MULTI_CASES, ids=lambda c: "P%d_N%d_K%d_g%d_B%d_cs%d_%s" % ((len(c[0]),) + c[1:]))
+def test_gemv_grouped_multi_matches_oracle(case):
+    Ms, N, K, g, B, cs, dt = case
+    say("bs_gemv_grouped_multi", case)
+    x = synth.random_x(sum(Ms) + N, N, B, dt)
+    projs, refs = [], []
+    for i, M in enumerate(Ms):
+        L, alpha, csb, _ = _inputs(max(M, 1), N, K, g, B, cs, dt, 900 + 31 * i + M)
+        L, alpha = L[:, :M], alpha[:, :M]
+        bits = bsg.bsg_logical_to_layout(to_dev(L.view(np.int32)), K, M, N) if M else \
+            torch.zeros(16, dtype=torch.int32, device=DEV)
+        projs.append((bits, M, f16_dev(_gm(alpha)) if M else torch.zeros(8, dtype=torch.int16, device=DEV),
+                      f16_dev(csb) if cs else None, None))
+        refs.append((L, alpha, csb))
+    ys = bsg.bs_gemv_grouped_multi(projs, K, N, g, x_dev(x, dt))
+    torch.cuda.synchronize()
+    for (L, alpha, csb), y, M in zip(refs, ys, Ms):
+        if M == 0:
+            continue
+        ref = oracle.sign_gemv_grouped(L, K, M, N, g, alpha, x, csb)
+        check_close(y.cpu().numpy(), ref, _tol(alpha, csb, x, g) + 1e-9, "grouped multi %s M=%d" % (case[1:], M))
+
+
+def test_gemv_grouped_multi_accumulates():
+    Ms, N, K, g = (256, 64, 64), 1024, 2, 128
+    say("bs_gemv_grouped_multi accumulate", Ms)
+    x = synth.random_x(5, N, 1, "bf16")
+    projs, refs = [], []
+    for i, M in enumerate(Ms):
+        L, alpha, csb, _ = _inputs(M, N, K, g, 1, True, "bf16", 950 + i)
+        y0 = np.random.default_rng(i).standard_normal((M, 1)).astype(np.float32)
+        bits = bsg.bsg_logical_to_layout(to_dev(L.view(np.int32)), K, M, N)
+        projs.append((bits, M, f16_dev(_gm(alpha)), f16_dev(csb), to_dev(y0)))
+        refs.append((L, alpha, csb, y0))
+    ys = bsg.bs_gemv_grouped_multi(projs, K, N, g, x_dev(x, "bf16"), accumulate=True)
+    torch.cuda.synchronize()
+    for (L, alpha, csb, y0), y, M in zip(refs, ys, Ms):
+        ref = oracle.sign_gemv_grouped(L, K, M, N, g, alpha, x, csb) + y0
+        check_close(y.cpu().numpy(), ref, _tol(alpha, csb, x, g) + 1e-6, "grouped multi accumulate M=%d" % M)
