@@ -116,6 +116,9 @@ GEMV_CASES = [
     (150, 1088, 2, 64, 1, True, "bf16"),
     (70, 576, 3, 64, 2, True, "f16"),
     (33, 1344, 1, 64, 1, False, "f32"),
+    # more workgroups than compute units: two workgroups per unit
+    (11008, 4096, 2, 128, 1, True, "f16"),
+    (6144, 2048, 3, 128, 1, True, "bf16"),
 ]
 
 

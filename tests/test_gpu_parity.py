@@ -63,6 +63,11 @@ GEMV_CASES = [
     (4, 130, 2080, 1, False, "f16", "normal"),
     (4, 200, 544, 1, False, "f32", "student_t3"),
     (3, 17000, 256, 1, False, "bf16", "normal"),
+    # more workgroups than compute units with more than half the LDS each: the
+    # planner halves the wavefronts so that two workgroups share a unit
+    (2, 6144, 4096, 1, True, "bf16", "normal"),
+    (2, 14336, 4096, 1, True, "f16", "normal"),
+    (3, 5000, 4096, 1, True, "bf16", "student_t3"),
 ]
 
 
