@@ -10,8 +10,13 @@ and adds the parity tolerance.  Each C function names the page passage it
 follows.  Functions whose results have no value printed on the pages are
 marked "parity unpinned" in DESIGN.md and below:
 
-* the least-squares column scale of the packer (``pack(with_colscale=True)``),
-* the protected-row selection rule (``salient_select``).
+* the least-squares column scale of the packer (``pack``, ``pack_grouped`` and
+  ``pack_hybrid`` with ``with_colscale=True``), pinned only to its closed-form
+  optimality,
+* the protected-row selection rule (``salient_select``),
+* the salient-column refinement of ``pack_hybrid`` as a refit of the residual
+  (a reading: the pages' equations for it are lost), pinned to its special
+  case with every column salient and to its effect on the error.
 """
 from __future__ import annotations
 
