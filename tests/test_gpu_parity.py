@@ -68,6 +68,7 @@ GEMV_CASES = [
     (2, 6144, 4096, 1, True, "bf16", "normal"),
     (2, 14336, 4096, 1, True, "f16", "normal"),
     (3, 5000, 4096, 1, True, "bf16", "student_t3"),
+    (2, 6144, 2048, 3, True, "bf16", "normal"),      # batch tile of 4 columns
 ]
 
 
