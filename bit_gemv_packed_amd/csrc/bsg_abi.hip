@@ -19,6 +19,8 @@ hipError_t launch_salient(const float* W, int M, int N, const float* xbar, int n
 hipError_t launch_salient_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s, int M, int N,
                                 const void* x, int xdt, int B, float* y, hipStream_t st);
 hipError_t launch_quantize(const void* x, int xdt, int N, int B, int8_t* xq, float* sx, hipStream_t st);
+hipError_t launch_lr_split(const float* z, const uint16_t* alpha_r, int r, int B, uint16_t* wh, uint16_t* wl,
+                           hipStream_t st);
 hipError_t launch_layout(const uint32_t* src, int K, int M, int N, uint32_t* dst, bool to_layout, hipStream_t st);
 size_t fit_workspace_bytes(int M, int N, int r);
 hipError_t launch_binlr_fit(const float* W, int M, int N, int r, int rounds, const uint32_t* v_init,
@@ -56,7 +58,11 @@ bsg_status hip_status(hipError_t e) {
 }
 
 // binlr workspace: z, fp32 [r][B]
-size_t binlr_ws(int r, int B) { return align_up((size_t)r * B * 4, 256); }
+// binlr workspace: z, fp32 [r][B]; for B >= 4 (the matrix-core expansion)
+// also the bf16 halves of alpha_r (.) z, [r][B] each
+size_t binlr_ws(int r, int B) {
+  return align_up((size_t)r * B * 4, 256) + (B >= 4 ? 2 * align_up((size_t)r * B * 2, 256) : 0);
+}
 
 bool xvec_ok(const void* x, const void* cs) {
   return (((uintptr_t)x) % 16) == 0 && (((uintptr_t)cs) % 8) == 0;
@@ -484,6 +490,52 @@ bsg_status bs_gemv_i8(const uint32_t* bits, int K, int M, int N, const float* al
   return hip_status(launch_prod_i8(a, p, (hipStream_t)stream));
 }
 
+// The low-rank correction on the matrix cores (B >= 4 columns of 16-bit x,
+// workspace of binlr_ws(r, B) bytes):
+//   z' = V x (fp32), w = alpha_r (.) z' split as w_hi + w_lo (bf16 each, 16
+//   significant bits together), y += U w_hi, y += U w_lo.
+// The products with the bf16 halves are exact and the sums fp32: the split's
+// 2^-16 relative rounding is the only error beyond fp32 sums.
+static hipError_t lowrank_mfma(const uint32_t* U_bits, const uint32_t* V_bits, const uint16_t* alpha_r, int r,
+                               int M, int N, const void* x, int xdt, int B, float* y, void* workspace,
+                               hipStream_t st) {
+  float* z = (float*)workspace;
+  uint16_t* wh = (uint16_t*)((char*)workspace + align_up((size_t)r * B * 4, 256));
+  uint16_t* wl = (uint16_t*)((char*)wh + align_up((size_t)r * B * 2, 256));
+  ProdArgs v{};
+  v.bits = V_bits;
+  v.x = x;
+  v.y = z;
+  v.plane = plane_words(r, N / 32);
+  v.K = 1;
+  v.M = r;
+  v.N = N;
+  v.ND = N / 32;
+  v.B = B;
+  v.xdt = xdt;
+  v.accumulate = 0;
+  hipError_t e = launch_prod_mfma(v, st);
+  if (e != hipSuccess) return e;
+  e = launch_lr_split(z, alpha_r, r, B, wh, wl, st);
+  if (e != hipSuccess) return e;
+  ProdArgs u{};
+  u.bits = U_bits;
+  u.x = wh;
+  u.y = y;
+  u.plane = plane_words(M, r / 32);
+  u.K = 1;
+  u.M = M;
+  u.N = r;
+  u.ND = r / 32;
+  u.B = B;
+  u.xdt = BSG_BF16;
+  u.accumulate = 1;
+  e = launch_prod_mfma(u, st);
+  if (e != hipSuccess) return e;
+  u.x = wl;
+  return launch_prod_mfma(u, st);
+}
+
 bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uint16_t* alpha_r, int r, int M,
                        int N, const void* x, int x_dtype, int B, float* y, void* workspace, size_t workspace_bytes,
                        void* stream) {
@@ -499,6 +551,8 @@ bsg_status binlr_apply(const uint32_t* U_bits, const uint32_t* V_bits, const uin
   if (!workspace || workspace_bytes < binlr_ws(r, B)) return BSG_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   float* z = (float*)workspace;
+  if (mfma_eligible(B, x_dtype, false)) return hip_status(lowrank_mfma(U_bits, V_bits, alpha_r, r, M, N, x, x_dtype, B, y,
+                                                                       workspace, st));
 
   // z' = V x: a one-base sign product with unit row scales
   ProdArgs v{};
@@ -563,6 +617,31 @@ bsg_status bsg_linear(const uint32_t* bits, int K, int M, int N, const float* al
   if (r > 0 && (!workspace || workspace_bytes < binlr_ws(r, B))) return BSG_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   float* z = (float*)workspace;
+
+  // B >= 4 columns of 16-bit x: the bases, the low-rank correction and the
+  // protected rows as separate launches on the matrix cores (the protected
+  // rows on their own kernel), each adding onto y
+  if (mfma_eligible(B, x_dtype, colscale != nullptr) ||
+      (colscale && !misaligned(colscale, 4) && mfma_cg_ok(B, x_dtype, x, true, 0, M))) {
+    ProdArgs a{};
+    a.bits = bits;
+    a.alpha = alpha;
+    a.colscale = colscale;
+    a.x = x;
+    a.y = y;
+    a.plane = plane_words(M, N / 32);
+    a.K = K;
+    a.M = M;
+    a.N = N;
+    a.ND = N / 32;
+    a.B = B;
+    a.xdt = x_dtype;
+    a.accumulate = accumulate ? 1 : 0;
+    hipError_t e = launch_prod_mfma(a, st);
+    if (e == hipSuccess && r > 0) e = lowrank_mfma(U_bits, V_bits, alpha_r, r, M, N, x, x_dtype, B, y, workspace, st);
+    if (e == hipSuccess && ns > 0) e = launch_salient_apply(rows, ns, q, s_f16, M, N, x, x_dtype, B, y, st);
+    return hip_status(e);
+  }
 
   if (r > 0) {  // z' = V x (unit row scales; alpha_r is applied in the expansion)
     ProdArgs v{};

@@ -77,6 +77,73 @@ __global__ void __launch_bounds__(1024) k_salient(const int32_t* __restrict__ ro
   }
 }
 
+// The same for several batch columns: workgroup (i, t) takes protected row i
+// and batch columns 16 t .. 16 t + 15; each thread takes columns n of x and
+// keeps 16 sums, loading the 16 values of x row n with two 16-byte loads
+// (VEC: 16-bit x, B % 8 == 0, x 16-byte aligned; else one load per value)
+// and q[i][n] once.  Each sum is reduced by a butterfly inside the
+// wavefront, then over the wavefronts in index order.  (Four protected rows
+// per workgroup, reading each row of x once for all four, measured 2.5x
+// slower: a quarter of the workgroups.)
+constexpr int kSalRows = 1;
+template <bool VEC>
+__global__ void __launch_bounds__(1024) k_salient_bt(const int32_t* __restrict__ rows, const int8_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ s, int ns, int M, int N,
+                                                   const void* __restrict__ x, int xdt, int B, float* __restrict__ y) {
+  __shared__ float red[16][kSalRows][16];
+  const int i0 = blockIdx.x * kSalRows, b0 = blockIdx.y * 16;
+  const int nr = min(kSalRows, ns - i0);  // protected rows of this workgroup
+  float acc[kSalRows][16];
+#pragma unroll
+  for (int r = 0; r < kSalRows; ++r)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[r][j] = 0.0f;
+  const bool full = VEC && b0 + 16 <= B;
+  for (int n = threadIdx.x; n < N; n += blockDim.x) {
+    float xv[16];
+    if (full) {
+      load8_x16(x, xdt, (size_t)n * B + b0, *(float(*)[8])xv);
+      load8_x16(x, xdt, (size_t)n * B + b0 + 8, *(float(*)[8])(xv + 8));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xv[j] = b0 + j < B ? load_x(x, xdt, (size_t)n * B + b0 + j) : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < kSalRows; ++r) {
+      if (r < nr) {
+        const float qn = (float)q[(size_t)(i0 + r) * N + n];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[r][j] = __builtin_fmaf(qn, xv[j], acc[r][j]);
+      }
+    }
+  }
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < kSalRows; ++r)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) acc[r][j] += __shfl_xor(acc[r][j], o);
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < kSalRows; ++r)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) red[wv][r][j] = acc[r][j];
+  }
+  __syncthreads();
+  const int r = threadIdx.x >> 4, j = threadIdx.x & 15;
+  if (threadIdx.x < kSalRows * 16 && r < nr && b0 + j < B) {
+    const int m = rows[i0 + r];
+    if (m >= 0 && m < M) {
+      const int W = blockDim.x >> 6;
+      float t = red[0][r][j];
+      for (int w = 1; w < W; ++w) t += red[w][r][j];
+      y[(size_t)m * B + b0 + j] += f16_bits_to_float(s[i0 + r]) * t;
+    }
+  }
+}
+
 // sx[b] = fp32(max_n |x| / 127); xq = clamp(rint_even(fp32(x / sx)), -127, 127).
 // One workgroup of 1024 threads per batch column.  VEC: one batch column of
 // 16-bit x, N % 8 == 0, x 16-byte and xq 8-byte aligned: 8 values per thread
@@ -185,7 +252,17 @@ static bool aligned(const void* p, size_t a) { return (((uintptr_t)p) % a) == 0;
 
 hipError_t launch_salient_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s, int M, int N,
                                 const void* x, int xdt, int B, float* y, hipStream_t st) {
-  const bool vec = B == 1 && xdt != BSG_F32 && N % 16 == 0 && aligned(q, 16) && aligned(x, 16);
+  if (B > 1) {  // a workgroup per protected row and 16 batch columns
+    const bool vec = xdt != BSG_F32 && B % 8 == 0 && aligned(x, 16);
+    const dim3 grid((ns + kSalRows - 1) / kSalRows, (B + 15) / 16);
+    const int threads = std::min(1024, std::max(64, (N / 4 + 63) / 64 * 64));  // about 4 columns each
+    if (vec)
+      hipLaunchKernelGGL(k_salient_bt<true>, grid, dim3(threads), 0, st, rows, q, s, ns, M, N, x, xdt, B, y);
+    else
+      hipLaunchKernelGGL(k_salient_bt<false>, grid, dim3(threads), 0, st, rows, q, s, ns, M, N, x, xdt, B, y);
+    return hipGetLastError();
+  }
+  const bool vec = xdt != BSG_F32 && N % 16 == 0 && aligned(q, 16) && aligned(x, 16);
   const int threads = std::min(1024, std::max(64, (N / (vec ? 16 : 1) + 63) / 64 * 64));
   if (vec)
     hipLaunchKernelGGL(k_salient<true>, dim3(ns), dim3(threads), 0, st, rows, q, s, M, N, x, xdt, B, y);
@@ -213,6 +290,31 @@ hipError_t launch_layout(const uint32_t* src, int K, int M, int N, uint32_t* dst
                        dst);
   else
     hipLaunchKernelGGL(k_from_layout, dim3(grid_for(total, 256)), dim3(256), 0, st, src, K, M, ND, plane, dst);
+  return hipGetLastError();
+}
+
+// The low-rank expansion's activations for the matrix cores: w = alpha_r (.)
+// z' in fp32 (z' [r][B], alpha_r fp16 [r]), split into two bf16 arrays with
+// w_hi = bf16(w) and w_lo = bf16(w - w_hi) (round to nearest even each), so
+// that w_hi + w_lo carries 16 significant bits of w.
+__global__ void k_lr_split(const float* __restrict__ z, const uint16_t* __restrict__ alpha_r, int n, int B,
+                           uint16_t* __restrict__ wh, uint16_t* __restrict__ wl) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const float w = z[i] * f16_bits_to_float(alpha_r[i / B]);
+    const __bf16 h = (__bf16)w;
+    const __bf16 l = (__bf16)(w - (float)h);
+    uint16_t hb, lb;
+    __builtin_memcpy(&hb, &h, 2);
+    __builtin_memcpy(&lb, &l, 2);
+    wh[i] = hb;
+    wl[i] = lb;
+  }
+}
+
+hipError_t launch_lr_split(const float* z, const uint16_t* alpha_r, int r, int B, uint16_t* wh, uint16_t* wl,
+                           hipStream_t st) {
+  const int n = r * B;
+  hipLaunchKernelGGL(k_lr_split, dim3(grid_for((size_t)n, 256)), dim3(256), 0, st, z, alpha_r, n, B, wh, wl);
   return hipGetLastError();
 }
 

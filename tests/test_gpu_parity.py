@@ -203,7 +203,9 @@ def test_quantize_i8_bit_exact():
 
 # ------------------------------------------------------------------ low rank
 LR_CASES = [(32, 256, 256, 1, "f32"), (512, 5120, 5120, 1, "bf16"), (64, 100, 96, 3, "f16"),
-            (512, 1000, 2048, 16, "bf16"), (32, 1, 32, 1, "f32")]
+            (512, 1000, 2048, 16, "bf16"), (32, 1, 32, 1, "f32"),
+            # B >= 4 columns of 16-bit x: the matrix cores (z in bf16 halves)
+            (96, 300, 544, 4, "f16"), (512, 2000, 5120, 20, "bf16"), (32, 70, 96, 6, "bf16")]
 
 
 @pytest.mark.parametrize("case", LR_CASES, ids=lambda c: "r%d_M%d_N%d_B%d_%s" % c)
@@ -263,6 +265,12 @@ LINEAR_CASES = [
     (2, 700, 4096, 2, False, "bf16", 0, 7),
     (2, 17000, 512, 1, False, "bf16", 128, 170),
     (2, 129, 1056, 3, True, "bf16", 32, 0),
+    # B >= 4 columns of 16-bit x: bases, correction and protected rows as
+    # separate matrix-core launches
+    (2, 1000, 2048, 16, False, "bf16", 128, 10),
+    (3, 300, 544, 8, True, "f16", 64, 3),         # fp16 column scales on the matrix cores
+    (5, 130, 1024, 4, False, "f16", 32, 0),       # two launches of bases
+    (2, 2000, 5120, 20, False, "bf16", 512, 20),  # two batch launches
 ]
 
 
