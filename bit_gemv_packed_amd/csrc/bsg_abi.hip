@@ -19,8 +19,6 @@ hipError_t launch_salient(const float* W, int M, int N, const float* xbar, int n
 hipError_t launch_salient_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s, int M, int N,
                                 const void* x, int xdt, int B, float* y, hipStream_t st);
 hipError_t launch_quantize(const void* x, int xdt, int N, int B, int8_t* xq, float* sx, hipStream_t st);
-hipError_t launch_lr_split(const float* z, const uint16_t* alpha_r, int r, int B, uint16_t* wh, uint16_t* wl,
-                           hipStream_t st);
 hipError_t launch_layout(const uint32_t* src, int K, int M, int N, uint32_t* dst, bool to_layout, hipStream_t st);
 size_t fit_workspace_bytes(int M, int N, int r);
 hipError_t launch_binlr_fit(const float* W, int M, int N, int r, int rounds, const uint32_t* v_init,
@@ -491,21 +489,20 @@ bsg_status bs_gemv_i8(const uint32_t* bits, int K, int M, int N, const float* al
 }
 
 // The low-rank correction on the matrix cores (B >= 4 columns of 16-bit x,
-// workspace of binlr_ws(r, B) bytes):
-//   z' = V x (fp32), w = alpha_r (.) z' split as w_hi + w_lo (bf16 each, 16
-//   significant bits together), y += U w_hi, y += U w_lo.
+// workspace of binlr_ws(r, B) bytes), two launches:
+//   z' = V x, written as w_hi = bf16(w), w_lo = bf16(w - w_hi) for
+//   w = alpha_r (.) z' (16 significant bits together), then
+//   y += U w_hi + U w_lo (two passes over U's tiles in one launch).
 // The products with the bf16 halves are exact and the sums fp32: the split's
 // 2^-16 relative rounding is the only error beyond fp32 sums.
 static hipError_t lowrank_mfma(const uint32_t* U_bits, const uint32_t* V_bits, const uint16_t* alpha_r, int r,
                                int M, int N, const void* x, int xdt, int B, float* y, void* workspace,
                                hipStream_t st) {
-  float* z = (float*)workspace;
   uint16_t* wh = (uint16_t*)((char*)workspace + align_up((size_t)r * B * 4, 256));
   uint16_t* wl = (uint16_t*)((char*)wh + align_up((size_t)r * B * 2, 256));
   ProdArgs v{};
   v.bits = V_bits;
   v.x = x;
-  v.y = z;
   v.plane = plane_words(r, N / 32);
   v.K = 1;
   v.M = r;
@@ -513,14 +510,15 @@ static hipError_t lowrank_mfma(const uint32_t* U_bits, const uint32_t* V_bits, c
   v.ND = N / 32;
   v.B = B;
   v.xdt = xdt;
-  v.accumulate = 0;
+  v.split_hi = wh;
+  v.split_lo = wl;
+  v.split_scale = alpha_r;
   hipError_t e = launch_prod_mfma(v, st);
-  if (e != hipSuccess) return e;
-  e = launch_lr_split(z, alpha_r, r, B, wh, wl, st);
   if (e != hipSuccess) return e;
   ProdArgs u{};
   u.bits = U_bits;
   u.x = wh;
+  u.x2 = wl;
   u.y = y;
   u.plane = plane_words(M, r / 32);
   u.K = 1;
@@ -530,9 +528,6 @@ static hipError_t lowrank_mfma(const uint32_t* U_bits, const uint32_t* V_bits, c
   u.B = B;
   u.xdt = BSG_BF16;
   u.accumulate = 1;
-  e = launch_prod_mfma(u, st);
-  if (e != hipSuccess) return e;
-  u.x = wl;
   return launch_prod_mfma(u, st);
 }
 

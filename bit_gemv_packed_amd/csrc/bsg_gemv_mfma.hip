@@ -13,9 +13,11 @@ bool mfma_eligible(int B, int xdt, bool colscale) {
   return B >= 4 && !colscale && (xdt == BSG_BF16 || xdt == BSG_F16);
 }
 
-// Instances with column or group scales (bsg_gemv_mfma_cg.hip).
+// Instances with column or group scales (bsg_gemv_mfma_cg.hip), and the
+// one-base instances of the batched low-rank expansion (bsg_gemv_mfma_ex.hip).
 hipError_t dispatch_mfma_cg(const ProdArgs& a, int RT, int KM, int XT, int VW, int CG, const ProdPlan& p,
                             hipStream_t st);
+hipError_t dispatch_mfma_ex(const ProdArgs& a, int RT, int XT, int VW, int EX, const ProdPlan& p, hipStream_t st);
 
 static hipError_t dispatch_mfma(const ProdArgs& a, int RT, int KM, int XT, int VW, int nwg, int W, size_t lds,
                                 hipStream_t st) {
@@ -92,7 +94,9 @@ hipError_t launch_prod_mfma(const ProdArgs& a0, hipStream_t st) {
   const int VW = mfma_vw(a0.B, a0.x);
   const bool multi = a0.np > 1;
   const int CG = (a0.colscale ? 1 : 0) | (a0.gsw ? 2 : 0);
+  const int EX = (a0.x2 ? 1 : 0) | (a0.split_hi ? 2 : 0);
   if (multi && VW < 4) return hipErrorInvalidConfiguration;
+  if (EX && (multi || CG || a0.K != 1)) return hipErrorInvalidConfiguration;
   if (CG && (multi || !mfma_cg_ok(a0.B, a0.xdt, a0.x, a0.colscale != nullptr, a0.gsw, a0.M)))
     return hipErrorInvalidConfiguration;
   int mt = a0.M;
@@ -147,12 +151,12 @@ hipError_t launch_prod_mfma(const ProdArgs& a0, hipStream_t st) {
       ProdArgs a = as;
       a.b0 = b0;
       hipError_t e;
-      if (CG) {
+      if (CG || EX) {
         ProdPlan p{};
         p.nwg = nwg;
         p.W = W;
         p.lds = lds;
-        e = dispatch_mfma_cg(a, RT, KM, XT, VW, CG, p, st);
+        e = CG ? dispatch_mfma_cg(a, RT, KM, XT, VW, CG, p, st) : dispatch_mfma_ex(a, RT, XT, VW, EX, p, st);
       } else {
         e = dispatch_mfma(a, RT, KM, XT, VW, nwg, W, lds, st);
       }

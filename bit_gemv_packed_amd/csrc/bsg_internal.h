@@ -133,6 +133,13 @@ struct ProdArgs {
   // workgroup w works for the last projection p with proj[p].wg0 <= w.
   int np;
   ProjDesc proj[kMaxProj];
+  // Batched low-rank expansion on the matrix cores (NULL when unused): a
+  // second activation array summed into the same product, and the split
+  // output hi/lo = bf16 halves of split_scale[m] * y[m][b]
+  const void* x2;
+  uint16_t* split_hi;
+  uint16_t* split_lo;
+  const uint16_t* split_scale;
 };
 
 hipError_t launch_prod_f(const ProdArgs& a, const ProdPlan& p, hipStream_t s);

@@ -293,29 +293,4 @@ hipError_t launch_layout(const uint32_t* src, int K, int M, int N, uint32_t* dst
   return hipGetLastError();
 }
 
-// The low-rank expansion's activations for the matrix cores: w = alpha_r (.)
-// z' in fp32 (z' [r][B], alpha_r fp16 [r]), split into two bf16 arrays with
-// w_hi = bf16(w) and w_lo = bf16(w - w_hi) (round to nearest even each), so
-// that w_hi + w_lo carries 16 significant bits of w.
-__global__ void k_lr_split(const float* __restrict__ z, const uint16_t* __restrict__ alpha_r, int n, int B,
-                           uint16_t* __restrict__ wh, uint16_t* __restrict__ wl) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
-    const float w = z[i] * f16_bits_to_float(alpha_r[i / B]);
-    const __bf16 h = (__bf16)w;
-    const __bf16 l = (__bf16)(w - (float)h);
-    uint16_t hb, lb;
-    __builtin_memcpy(&hb, &h, 2);
-    __builtin_memcpy(&lb, &l, 2);
-    wh[i] = hb;
-    wl[i] = lb;
-  }
-}
-
-hipError_t launch_lr_split(const float* z, const uint16_t* alpha_r, int r, int B, uint16_t* wh, uint16_t* wl,
-                           hipStream_t st) {
-  const int n = r * B;
-  hipLaunchKernelGGL(k_lr_split, dim3(grid_for((size_t)n, 256)), dim3(256), 0, st, z, alpha_r, n, B, wh, wl);
-  return hipGetLastError();
-}
-
 }  // namespace bsg

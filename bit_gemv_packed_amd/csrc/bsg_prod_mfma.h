@@ -132,8 +132,12 @@ struct MfTile {
 // XT: 1 bf16, 2 fp16 activations.  VW: batch values per x load (8, 4, 2 or
 // 1: B % VW == 0 and x aligned to 2 VW bytes).  MP = 1: the fused launch of
 // several projections (bs_gemv_multi).  CG: column scales (bit 0, fp16 x)
-// and group-wise row scales (bit 1), as above.
-template <int RT, int KM, int XT, int VW, int MP, int CG = 0>
+// and group-wise row scales (bit 1), as above.  EX bit 0: the tiles again
+// with a.x2 in place of x, summed into the same result (the two
+// bf16 halves of the low-rank expansion's activations); EX bit 1: instead of
+// y, write the bf16 halves hi = bf16(w), lo = bf16(w - hi) of w = s[m] * y
+// (s = a.split_scale fp16, outputs a.split_hi / a.split_lo, [M][B]).
+template <int RT, int KM, int XT, int VW, int MP, int CG = 0, int EX = 0>
 __global__ void __launch_bounds__(64 * mfma_max_waves(RT, KM, VW, CG)) k_prod_mfma(ProdArgs a) {
   asm volatile("" ::"s"(a.bits), "s"(a.alpha), "s"(a.x), "s"(a.y), "s"(a.plane), "s"(a.K), "s"(a.M), "s"(a.N),
                "s"(a.ND), "s"(a.B), "s"(a.b0), "s"(a.accumulate), "s"(a.NCH), "s"(a.x_bytes), "s"(a.al_bytes));
@@ -190,7 +194,7 @@ __global__ void __launch_bounds__(64 * mfma_max_waves(RT, KM, VW, CG)) k_prod_mf
   for (int q = 0; q < NL; ++q) xo[q] = bb + q * VW < a.B ? (uint32_t)(nl * a.B + bb + q * VW) * 2u : kOut;
   const uint32_t xstep = 64u * (uint32_t)a.B;  // bytes of x per step
 
-  auto load_tile = [&](int t, MfTile<RT, KM, CG>& d) {
+  auto load_tile = [&](int t, MfTile<RT, KM, CG>& d, const rsrc_t& xr) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -214,19 +218,19 @@ __global__ void __launch_bounds__(64 * mfma_max_waves(RT, KM, VW, CG)) k_prod_mf
 #pragma unroll
       for (int q = 0; q < NL; ++q) {
         if (VW == 8) {
-          const uint4 v = ld128(xs, xo[q] + so);
+          const uint4 v = ld128(xr, xo[q] + so);
           d.x[j][0] = v.x;
           d.x[j][1] = v.y;
           d.x[j][2] = v.z;
           d.x[j][3] = v.w;
         } else if (VW == 4) {
-          const uint2 v = ld64(xs, xo[q] + so);
+          const uint2 v = ld64(xr, xo[q] + so);
           d.x[j][2 * q] = v.x;
           d.x[j][2 * q + 1] = v.y;
         } else if (VW == 2) {
-          d.x[j][q] = ld32(xs, xo[q] + so);
+          d.x[j][q] = ld32(xr, xo[q] + so);
         } else {
-          const uint32_t h = ld16(xs, xo[q] + so);
+          const uint32_t h = ld16(xr, xo[q] + so);
           d.x[j][q >> 1] = (q & 1) ? (d.x[j][q >> 1] | (h << 16)) : h;
         }
       }
@@ -305,15 +309,35 @@ __global__ void __launch_bounds__(64 * mfma_max_waves(RT, KM, VW, CG)) k_prod_mf
   const int NT = a.NCH >> 2;
   const int tb = wv * NT;
   MfTile<RT, KM, CG> ta, tc;
-  load_tile(tb, ta);
-  int t = 0;
-  for (; t + 2 <= NT; t += 2) {
-    load_tile(tb + t + 1, tc);
-    run_tile(ta);
-    load_tile(tb + min(t + 2, NT - 1), ta);  // past the last tile: re-read it (a cache hit)
-    run_tile(tc);
+  if constexpr ((EX & 1) == 0) {
+    load_tile(tb, ta, xs);
+    int t = 0;
+    for (; t + 2 <= NT; t += 2) {
+      load_tile(tb + t + 1, tc, xs);
+      run_tile(ta);
+      load_tile(tb + min(t + 2, NT - 1), ta, xs);  // past the last tile: re-read it (a cache hit)
+      run_tile(tc);
+    }
+    if (t < NT) run_tile(ta);
+  } else {
+    // 2 NT steps: the tiles with x, then the same sign tiles again with x2,
+    // summed into the same accumulators
+    const rsrc_t xs2 = make_rsrc(a.x2, a.x_bytes);
+    auto load_v = [&](int v, MfTile<RT, KM, CG>& d) {
+      const bool second = v >= NT;
+      load_tile(tb + (second ? v - NT : v), d, second ? xs2 : xs);
+    };
+    const int NV = 2 * NT;
+    load_v(0, ta);
+    int v = 0;
+    for (; v + 2 <= NV; v += 2) {
+      load_v(v + 1, tc);
+      run_tile(ta);
+      load_v(min(v + 2, NV - 1), ta);
+      run_tile(tc);
+    }
+    if (v < NV) run_tile(ta);
   }
-  if (t < NT) run_tile(ta);
 
   // row scales: lane holds C rows 4 g + i, batch column r16, of each row tile
   const rsrc_t als = make_rsrc(a.alpha, a.al_bytes);
@@ -339,7 +363,15 @@ __global__ void __launch_bounds__(64 * mfma_max_waves(RT, KM, VW, CG)) k_prod_mf
     if (m < a.M && b < a.B) {
       const float sum = sum_waves(red + (rt * 16 + row) * 16 + col, RT * 256, W);
       const size_t yi = (size_t)m * a.B + b;
-      a.y[yi] = (a.accumulate ? a.y[yi] : 0.0f) + sum;
+      if (EX & 2) {
+        const float w = sum * f16_bits_to_float(a.split_scale[m]);
+        const __bf16 hi = (__bf16)w;
+        const __bf16 lo = (__bf16)(w - (float)hi);
+        __builtin_memcpy(a.split_hi + yi, &hi, 2);
+        __builtin_memcpy(a.split_lo + yi, &lo, 2);
+      } else {
+        a.y[yi] = (a.accumulate ? a.y[yi] : 0.0f) + sum;
+      }
     }
   }
 }
