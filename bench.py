@@ -347,11 +347,14 @@ def run_rows(steps, warmup):
     del P, x
     torch.cuda.empty_cache()
 
-    # a4, a5: the fused layer (bases + binary low-rank + protected int8 rows) and its parts
-    for name, M, N, K, r, frac in [("5120x5120 K=3 r=512", 5120, 5120, 3, 512, 0.0),
-                                   ("13824x5120 r=512 1% rows", 13824, 5120, 2, 512, 0.01),
-                                   ("5120x13824 r=512 1% rows", 5120, 13824, 2, 512, 0.01),
-                                   ("28672x8192 r=512 1% rows", 28672, 8192, 2, 512, 0.01)]:
+    # a4, a5: the fused layer (bases + binary low-rank + protected int8 rows) and its parts; at
+    # B = 16 columns of bf16 x every part runs on the matrix cores except the protected rows
+    for name, M, N, K, r, frac, B in [("5120x5120 K=3 r=512", 5120, 5120, 3, 512, 0.0, 1),
+                                      ("13824x5120 r=512 1% rows", 13824, 5120, 2, 512, 0.01, 1),
+                                      ("5120x13824 r=512 1% rows", 5120, 13824, 2, 512, 0.01, 1),
+                                      ("28672x8192 r=512 1% rows", 28672, 8192, 2, 512, 0.01, 1),
+                                      ("13824x5120 r=512 1% rows B=16", 13824, 5120, 2, 512, 0.01, 16),
+                                      ("28672x8192 r=512 1% rows B=16", 28672, 8192, 2, 512, 0.01, 16)]:
         ns = synth.n_salient(M, frac) if frac else 0
         wb = K * M * N // 8 + 4 * K * M
         lrb = r * N // 8 + M * r // 8 + 2 * r
@@ -366,21 +369,22 @@ def run_rows(steps, warmup):
             if ns else None
         q = torch.randint(-127, 128, (n, ns, N), dtype=torch.int8, device=dev) if ns else None
         sv = (torch.rand((n, ns), device=dev) * 1e-3).half().view(torch.int16) if ns else None
-        x = xs(N, 1, n)
-        y = torch.empty((n, M, 1), device=dev)
-        ws = bsg.new_workspace(bsg.lib().bsg_linear_workspace_bytes(r, 1), dev)
+        x = xs(N, B, n)
+        y = torch.empty((n, M, B), device=dev)
+        ws = bsg.new_workspace(bsg.lib().bsg_linear_workspace_bytes(r, B), dev)
+        launches = "2 launches" if B == 1 else "matrix cores"
 
         def step(i):
             c = i % n
             bsg.bsg_linear(bits[c], K, M, N, alpha[c], x[c], lowrank=(U[c], V[c], ar[c], r),
                            salient=(rows[c], q[c], sv[c]) if ns else None, y=y[c], workspace=ws)
-        emit("a2-a5", "bsg_linear (2 launches)", name, _graph_us(step, steps, warmup), wb + lrb + sb + 2 * N,
-             K=K, r=r, ns=ns)
+        emit("a2-a5", "bsg_linear (%s)" % launches, name, _graph_us(step, steps, warmup),
+             wb + lrb + sb + 2 * N * B, K=K, r=r, ns=ns, B=B)
         step = lambda i: bsg.binlr_apply(U[i % n], V[i % n], ar[i % n], r, M, N, x[i % n], y[i % n], workspace=ws)
-        emit("a4", "binlr_apply alone (2 launches)", name, _graph_us(step, steps, warmup), lrb + 2 * N, r=r)
+        emit("a4", "binlr_apply alone (2 launches)", name, _graph_us(step, steps, warmup), lrb + 2 * N * B, r=r, B=B)
         if ns:
             step = lambda i: bsg.salient_int8_apply(rows[i % n], q[i % n], sv[i % n], M, N, x[i % n], y[i % n])
-            emit("a5", "salient_int8_apply alone", name, _graph_us(step, steps, warmup), sb + 2 * N, ns=ns)
+            emit("a5", "salient_int8_apply alone", name, _graph_us(step, steps, warmup), sb + 2 * N * B, ns=ns, B=B)
         del bits, alpha, U, V, ar, rows, q, sv, x, y, ws
         torch.cuda.empty_cache()
 

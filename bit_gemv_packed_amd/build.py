@@ -18,7 +18,8 @@ OBJDIR = os.path.join(ROOT, "_build", "bsg")
 LIB = os.path.join(HERE, "libbsg.so")
 SOURCES = ["bsg_abi.hip", "bsg_gemv.hip", "bsg_gemv_mfma.hip", "bsg_gemv_i8.hip", "bsg_pack.hip", "bsg_misc.hip",
            "bsg_lrfit.hip", "bsg_gemv_gs.hip",
-           "bsg_gemv_mfma_cg.hip", "bsg_vcm_mfma.hip", "bsg_gemv_mfma_ex.hip"]
+           "bsg_gemv_mfma_cg.hip", "bsg_vcm_mfma.hip", "bsg_gemv_mfma_ex.hip",
+           "bsg_salient_mfma.hip"]
 ARCH = os.environ.get("BSG_OFFLOAD_ARCH", "gfx950")
 
 CFLAGS = [

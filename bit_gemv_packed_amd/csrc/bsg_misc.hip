@@ -25,15 +25,19 @@ __device__ inline float block_reduce(float v, float* red) {
   return t;
 }
 
-// 8 consecutive 16-bit x values (one aligned 16-byte load) -> fp32
-__device__ inline void load8_x16(const void* x, int xdt, size_t i, float (&v)[8]) {
-  const uint4 u = *(const uint4*)((const uint16_t*)x + i);
+// 8 16-bit x values in one 16-byte word -> fp32
+__device__ inline void cvt8_x16(const uint4 u, int xdt, float (&v)[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint16_t h = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
     v[j] = xdt == BSG_BF16 ? bf16_bits_to_float(h) : f16_bits_to_float(h);
   }
+}
+
+// 8 consecutive 16-bit x values (one aligned 16-byte load) -> fp32
+__device__ inline void load8_x16(const void* x, int xdt, size_t i, float (&v)[8]) {
+  cvt8_x16(*(const uint4*)((const uint16_t*)x + i), xdt, v);
 }
 
 // y[rows[i], b] += s_i * sum_n q[i][n] * x[n, b]   (BiSCo "Sensitivity
@@ -79,67 +83,78 @@ __global__ void __launch_bounds__(1024) k_salient(const int32_t* __restrict__ ro
 
 // The same for several batch columns: workgroup (i, t) takes protected row i
 // and batch columns 16 t .. 16 t + 15; each thread takes columns n of x and
-// keeps 16 sums, loading the 16 values of x row n with two 16-byte loads
-// (VEC: 16-bit x, B % 8 == 0, x 16-byte aligned; else one load per value)
-// and q[i][n] once.  Each sum is reduced by a butterfly inside the
+// keeps 16 sums.  VEC (16-bit x, B % 8 == 0, x 16-byte aligned), all 16
+// columns in range: a thread issues the loads of up to kSalCols columns (two
+// 16-byte loads of the x row, one q byte each) before any product, so a
+// row of up to kSalCols * 1024 columns costs one round of memory latency (a
+// loop that waited for each column's loads cost about 2 us per column on
+// 1024 threads); columns past N re-read column N - 1 with weight 0.  Else
+// one load per value.  Each sum is reduced by a butterfly inside the
 // wavefront, then over the wavefronts in index order.  (Four protected rows
 // per workgroup, reading each row of x once for all four, measured 2.5x
 // slower: a quarter of the workgroups.)
-constexpr int kSalRows = 1;
+constexpr int kSalCols = 8;
 template <bool VEC>
 __global__ void __launch_bounds__(1024) k_salient_bt(const int32_t* __restrict__ rows, const int8_t* __restrict__ q,
                                                    const uint16_t* __restrict__ s, int ns, int M, int N,
                                                    const void* __restrict__ x, int xdt, int B, float* __restrict__ y) {
-  __shared__ float red[16][kSalRows][16];
-  const int i0 = blockIdx.x * kSalRows, b0 = blockIdx.y * 16;
-  const int nr = min(kSalRows, ns - i0);  // protected rows of this workgroup
-  float acc[kSalRows][16];
+  __shared__ float red[16][16];
+  const int i = blockIdx.x, b0 = blockIdx.y * 16;
+  const int8_t* qi = q + (size_t)i * N;
+  float acc[16];
 #pragma unroll
-  for (int r = 0; r < kSalRows; ++r)
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+  if (VEC && b0 + 16 <= B) {
+    for (int n0 = threadIdx.x; n0 < N; n0 += kSalCols * blockDim.x) {
+      uint4 xa[kSalCols], xb[kSalCols];
+      int qr[kSalCols];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[r][j] = 0.0f;
-  const bool full = VEC && b0 + 16 <= B;
-  for (int n = threadIdx.x; n < N; n += blockDim.x) {
-    float xv[16];
-    if (full) {
-      load8_x16(x, xdt, (size_t)n * B + b0, *(float(*)[8])xv);
-      load8_x16(x, xdt, (size_t)n * B + b0 + 8, *(float(*)[8])(xv + 8));
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) xv[j] = b0 + j < B ? load_x(x, xdt, (size_t)n * B + b0 + j) : 0.0f;
-    }
-#pragma unroll
-    for (int r = 0; r < kSalRows; ++r) {
-      if (r < nr) {
-        const float qn = (float)q[(size_t)(i0 + r) * N + n];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[r][j] = __builtin_fmaf(qn, xv[j], acc[r][j]);
+      for (int u = 0; u < kSalCols; ++u) {
+        const int nc = min(n0 + u * (int)blockDim.x, N - 1);
+        const uint16_t* xr = (const uint16_t*)x + (size_t)nc * B + b0;
+        xa[u] = *(const uint4*)xr;
+        xb[u] = *(const uint4*)(xr + 8);
+        qr[u] = qi[nc];
       }
+#pragma unroll
+      for (int u = 0; u < kSalCols; ++u) {
+        const float qn = n0 + u * (int)blockDim.x < N ? (float)qr[u] : 0.0f;
+        float xv[8];
+        cvt8_x16(xa[u], xdt, xv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(qn, xv[j], acc[j]);
+        cvt8_x16(xb[u], xdt, xv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[8 + j] = __builtin_fmaf(qn, xv[j], acc[8 + j]);
+      }
+    }
+  } else {
+    for (int n = threadIdx.x; n < N; n += blockDim.x) {
+      const float qn = (float)qi[n];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (b0 + j < B) acc[j] = __builtin_fmaf(qn, load_x(x, xdt, (size_t)n * B + b0 + j), acc[j]);
     }
   }
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int r = 0; r < kSalRows; ++r)
+  for (int j = 0; j < 16; ++j) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) acc[r][j] += __shfl_xor(acc[r][j], o);
-    }
+    for (int o = 32; o >= 1; o >>= 1) acc[j] += __shfl_xor(acc[j], o);
+  }
   if (lane == 0) {
 #pragma unroll
-    for (int r = 0; r < kSalRows; ++r)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) red[wv][r][j] = acc[r][j];
+    for (int j = 0; j < 16; ++j) red[wv][j] = acc[j];
   }
   __syncthreads();
-  const int r = threadIdx.x >> 4, j = threadIdx.x & 15;
-  if (threadIdx.x < kSalRows * 16 && r < nr && b0 + j < B) {
-    const int m = rows[i0 + r];
+  const int j = threadIdx.x;
+  if (j < 16 && b0 + j < B) {
+    const int m = rows[i];
     if (m >= 0 && m < M) {
       const int W = blockDim.x >> 6;
-      float t = red[0][r][j];
-      for (int w = 1; w < W; ++w) t += red[w][r][j];
-      y[(size_t)m * B + b0 + j] += f16_bits_to_float(s[i0 + r]) * t;
+      float t = red[0][j];
+      for (int w = 1; w < W; ++w) t += red[w][j];
+      y[(size_t)m * B + b0 + j] += f16_bits_to_float(s[i]) * t;
     }
   }
 }
@@ -250,12 +265,26 @@ static int grid_for(size_t n, int threads) {
 
 static bool aligned(const void* p, size_t a) { return (((uintptr_t)p) % a) == 0; }
 
+bool salient_mfma_ok(int ns, int N, const int8_t* q, const void* x, int xdt, int B);
+hipError_t launch_salient_mfma(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s, int M, int N,
+                               const void* x, int xdt, int B, float* y, hipStream_t st);
+
 hipError_t launch_salient_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s, int M, int N,
                                 const void* x, int xdt, int B, float* y, hipStream_t st) {
+  // Both batched kernels move about 13-14 bytes per clock into each compute
+  // unit, so the time follows the bytes of the busiest one: a workgroup per
+  // row reads x (32 N bytes per 16 batch columns) on each of up to 256
+  // compute units and twice that where a unit takes two rows; 16 rows per
+  // workgroup read x and 16 rows of q (48 N).  Measured at B = 16: 138 rows
+  // of 5120 take 8.0 us one per workgroup and 10.1 us on the matrix cores;
+  // 287 rows of 8192 take 16.7 and 14.6 us.
+  if (ns > 256 && salient_mfma_ok(ns, N, q, x, xdt, B))
+    return launch_salient_mfma(rows, ns, q, s, M, N, x, xdt, B, y, st);
   if (B > 1) {  // a workgroup per protected row and 16 batch columns
     const bool vec = xdt != BSG_F32 && B % 8 == 0 && aligned(x, 16);
-    const dim3 grid((ns + kSalRows - 1) / kSalRows, (B + 15) / 16);
-    const int threads = std::min(1024, std::max(64, (N / 4 + 63) / 64 * 64));  // about 4 columns each
+    const dim3 grid(ns, (B + 15) / 16);
+    // VEC: about kSalCols columns each, else about 4
+    const int threads = std::min(1024, std::max(64, (N / (vec ? kSalCols : 4) + 63) / 64 * 64));
     if (vec)
       hipLaunchKernelGGL(k_salient_bt<true>, grid, dim3(threads), 0, st, rows, q, s, ns, M, N, x, xdt, B, y);
     else

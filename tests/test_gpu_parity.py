@@ -230,21 +230,29 @@ def test_binlr_apply_matches_oracle(case):
 
 
 # ------------------------------------------------------------------ protected rows
-SAL_CASES = [(256, 256, 3, 1), (13824, 5120, 138, 1), (100, 100, 5, 2), (5120, 13824, 51, 16), (64, 32, 64, 1),
-             (64, 48, 3, 1), (300, 100, 7, 1), (5120, 13824, 51, 1)]
+# More than 256 protected rows, B % 8 == 0, N % 8 == 0 and 16-bit x: 16 protected rows per workgroup
+# on the matrix cores (ragged row tiles, half-empty and several batch tiles, partial and single
+# 128-column runs); otherwise one workgroup per row (hoisted loads when B % 8 == 0)
+SAL_CASES = [(256, 256, 3, 1, "bf16"), (13824, 5120, 138, 1, "bf16"), (100, 100, 5, 2, "bf16"),
+             (5120, 13824, 51, 16, "bf16"), (64, 32, 64, 1, "bf16"), (64, 48, 3, 1, "bf16"),
+             (300, 100, 7, 1, "bf16"), (5120, 13824, 51, 1, "bf16"), (13824, 5120, 138, 16, "bf16"),
+             (13824, 5120, 138, 16, "f16"), (300, 200, 20, 8, "bf16"), (64, 40, 17, 24, "f16"),
+             (100, 100, 5, 16, "bf16"), (200, 256, 9, 12, "f16"),
+             (28672, 8192, 287, 16, "bf16"), (2000, 520, 300, 16, "f16"), (1000, 4104, 270, 32, "bf16"),
+             (600, 40, 260, 8, "bf16"), (700, 100, 280, 16, "bf16")]
 
 
-@pytest.mark.parametrize("case", SAL_CASES, ids=lambda c: "M%d_N%d_ns%d_B%d" % c)
+@pytest.mark.parametrize("case", SAL_CASES, ids=lambda c: "M%d_N%d_ns%d_B%d_%s" % c)
 def test_salient_apply_matches_oracle(case):
-    M, N, ns, B = case
+    M, N, ns, B, dt = case
     say("salient_apply", case)
     g = np.random.default_rng(M + N + ns)
     rows = np.sort(g.choice(M, ns, replace=False)).astype(np.int32)
     q = g.integers(-127, 128, (ns, N)).astype(np.int8)
     s = g.uniform(1e-4, 1e-3, ns).astype(np.float16).view(np.uint16)
-    x = synth.random_x(M + N, N, B, "bf16", "student_t3")
+    x = synth.random_x(M + N, N, B, dt, "student_t3")
     y = torch.zeros((M, B), dtype=torch.float32, device=DEV)
-    bsg.salient_int8_apply(to_dev(rows), to_dev(q), f16_dev(s), M, N, x_dev(x, "bf16"), y)
+    bsg.salient_int8_apply(to_dev(rows), to_dev(q), f16_dev(s), M, N, x_dev(x, dt), y)
     torch.cuda.synchronize()
     ref = oracle.salient(rows, q, s, M, N, x)
     tol = oracle.tolerance(x, rows=rows, q=q, s_f16=s, M=M)
