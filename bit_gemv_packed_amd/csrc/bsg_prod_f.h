@@ -565,8 +565,10 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB, GS, XM), (KM <= 2 
   }
 
   // ---- fused protected rows: y[rows[i]] += s_i (q_i . x) (BiSCo-LLM,
-  // "Sensitivity Protection"); the workgroup's protected rows go
-  // round-robin over its wavefronts, each dot product over all 64 lanes
+  // "Sensitivity Protection"); each of the workgroup's protected rows is
+  // split into shares of 1024 columns over its first wavefronts (one round
+  // of loads for N <= 1024 W; the first wavefronts start first), and the
+  // shares meet in the workgroup's final sum of wavefront partials
   if (a.sal_n > 0) {
     const rsrc_t rs = make_rsrc(a.sal_rows, (size_t)a.sal_n * 4);
     const rsrc_t qs = make_rsrc(a.sal_q, (size_t)a.sal_n * a.N);
@@ -574,12 +576,16 @@ __global__ void __launch_bounds__(64 * prod_max_waves(KM, BB, GS, XM), (KM <= 2 
     const int m0 = (int)(blk * RW);
     const int i0 = lower_bound_rows(rs, a.sal_n, m0, lane);
     const int i1 = lower_bound_rows(rs, a.sal_n, m0 + RW, lane);
-    for (int i = i0 + wv; i < i1; i += a.W) {
+    // shares of 1024 columns (one load per lane), or 1024 times the fewest
+    // rounds that reach N over W wavefronts: the first wavefronts take them
+    const int span = 1024 * ((a.N + 1024 * a.W - 1) / (1024 * a.W));
+    const int c1 = min(a.N, (wv + 1) * span);
+    for (int i = i0; i < i1; ++i) {
       const int rr = __builtin_amdgcn_readfirstlane((int)ld32(rs, (uint32_t)i * 4u)) - m0;
       float dot[BB];
 #pragma unroll
       for (int b = 0; b < BB; ++b) dot[b] = 0.0f;
-      for (int n0 = lane * 16; n0 < a.N; n0 += 1024) {
+      for (int n0 = wv * span + lane * 16; n0 < c1; n0 += 1024) {
         const uint4 qv = ld128(qs, (uint32_t)((size_t)i * a.N + n0));
         const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
         if (XM != 0) {  // 16 aligned 16-bit activations: two 16-byte loads
