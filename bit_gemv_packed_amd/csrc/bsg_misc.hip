@@ -81,20 +81,11 @@ __global__ void __launch_bounds__(1024) k_salient(const int32_t* __restrict__ ro
   }
 }
 
-// The same for several batch columns: workgroup (i, t) takes protected row i
-// and batch columns 16 t .. 16 t + 15; each thread takes columns n of x and
-// keeps 16 sums.  VEC (16-bit x, B % 8 == 0, x 16-byte aligned), all 16
-// columns in range: a thread issues the loads of up to kSalCols columns (two
-// 16-byte loads of the x row, one q byte each) before any product, so a
-// row of up to kSalCols * 1024 columns costs one round of memory latency (a
-// loop that waited for each column's loads cost about 2 us per column on
-// 1024 threads); columns past N re-read column N - 1 with weight 0.  Else
-// one load per value.  Each sum is reduced by a butterfly inside the
-// wavefront, then over the wavefronts in index order.  (Four protected rows
-// per workgroup, reading each row of x once for all four, measured 2.5x
-// slower: a quarter of the workgroups.)
-constexpr int kSalCols = 8;
-template <bool VEC>
+// The same for several batch columns, any layout of x: workgroup (i, t)
+// takes protected row i and batch columns 16 t .. 16 t + 15; each thread
+// takes columns n of x, keeps 16 sums and loads each value on its own.
+// Each sum is reduced by a butterfly inside the wavefront, then over the
+// wavefronts in index order.
 __global__ void __launch_bounds__(1024) k_salient_bt(const int32_t* __restrict__ rows, const int8_t* __restrict__ q,
                                                    const uint16_t* __restrict__ s, int ns, int M, int N,
                                                    const void* __restrict__ x, int xdt, int B, float* __restrict__ y) {
@@ -104,37 +95,11 @@ __global__ void __launch_bounds__(1024) k_salient_bt(const int32_t* __restrict__
   float acc[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-  if (VEC && b0 + 16 <= B) {
-    for (int n0 = threadIdx.x; n0 < N; n0 += kSalCols * blockDim.x) {
-      uint4 xa[kSalCols], xb[kSalCols];
-      int qr[kSalCols];
+  for (int n = threadIdx.x; n < N; n += blockDim.x) {
+    const float qn = (float)qi[n];
 #pragma unroll
-      for (int u = 0; u < kSalCols; ++u) {
-        const int nc = min(n0 + u * (int)blockDim.x, N - 1);
-        const uint16_t* xr = (const uint16_t*)x + (size_t)nc * B + b0;
-        xa[u] = *(const uint4*)xr;
-        xb[u] = *(const uint4*)(xr + 8);
-        qr[u] = qi[nc];
-      }
-#pragma unroll
-      for (int u = 0; u < kSalCols; ++u) {
-        const float qn = n0 + u * (int)blockDim.x < N ? (float)qr[u] : 0.0f;
-        float xv[8];
-        cvt8_x16(xa[u], xdt, xv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = __builtin_fmaf(qn, xv[j], acc[j]);
-        cvt8_x16(xb[u], xdt, xv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[8 + j] = __builtin_fmaf(qn, xv[j], acc[8 + j]);
-      }
-    }
-  } else {
-    for (int n = threadIdx.x; n < N; n += blockDim.x) {
-      const float qn = (float)qi[n];
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (b0 + j < B) acc[j] = __builtin_fmaf(qn, load_x(x, xdt, (size_t)n * B + b0 + j), acc[j]);
-    }
+    for (int j = 0; j < 16; ++j)
+      if (b0 + j < B) acc[j] = __builtin_fmaf(qn, load_x(x, xdt, (size_t)n * B + b0 + j), acc[j]);
   }
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
@@ -155,6 +120,82 @@ __global__ void __launch_bounds__(1024) k_salient_bt(const int32_t* __restrict__
       float t = red[0][j];
       for (int w = 1; w < W; ++w) t += red[w][j];
       y[(size_t)m * B + b0 + j] += f16_bits_to_float(s[i]) * t;
+    }
+  }
+}
+
+// Four protected rows and four batch columns per workgroup (16-bit x, B % 4
+// == 0, x 8-byte aligned): 16 sums per thread, one 8-byte x load and four
+// q bytes per column n.  A thread issues the loads of up to kSalCols
+// columns before any product, so a row of up to kSalCols * 1024 columns
+// costs one round of memory latency (a loop that waited for each column's
+// loads cost about 2 us per column on 1024 threads); columns past N re-read
+// column N - 1 and rows past ns re-read row ns - 1, with weight 0.
+constexpr int kSalCols = 8;
+template <int R>
+__global__ void __launch_bounds__(1024) k_salient_rb(const int32_t* __restrict__ rows, const int8_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ s, int ns, int M, int N,
+                                                   const void* __restrict__ x, int xdt, int B, float* __restrict__ y) {
+  constexpr int BC = 16 / R;  // batch columns per workgroup (4: one 8-byte load)
+  static_assert(BC == 4, "one 8-byte x load per column");
+  __shared__ float red[16][16];
+  const int i0 = blockIdx.x * R, b0 = blockIdx.y * BC;
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+  const int8_t* qr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) qr[r] = q + (size_t)min(i0 + r, ns - 1) * N;
+  for (int n0 = threadIdx.x; n0 < N; n0 += kSalCols * blockDim.x) {
+    uint2 xv[kSalCols];
+    int qv[kSalCols][R];
+#pragma unroll
+    for (int u = 0; u < kSalCols; ++u) {
+      const int nc = min(n0 + u * (int)blockDim.x, N - 1);
+      xv[u] = *(const uint2*)((const uint16_t*)x + (size_t)nc * B + b0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) qv[u][r] = qr[r][nc];
+    }
+#pragma unroll
+    for (int u = 0; u < kSalCols; ++u) {
+      const bool in = n0 + u * (int)blockDim.x < N;
+      const uint32_t w[2] = {xv[u].x, xv[u].y};
+      float xf[BC];
+#pragma unroll
+      for (int c = 0; c < BC; ++c) {
+        const uint16_t h = (uint16_t)(w[c >> 1] >> (16 * (c & 1)));
+        xf[c] = xdt == BSG_BF16 ? bf16_bits_to_float(h) : f16_bits_to_float(h);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float qf = in && i0 + r < ns ? (float)qv[u][r] : 0.0f;
+#pragma unroll
+        for (int c = 0; c < BC; ++c) acc[r * BC + c] = __builtin_fmaf(qf, xf[c], acc[r * BC + c]);
+      }
+    }
+  }
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc[j] += __shfl_xor(acc[j], o);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) red[wv][j] = acc[j];
+  }
+  __syncthreads();
+  const int j = threadIdx.x;
+  if (j < 16) {
+    const int i = i0 + j / BC, b = b0 + j % BC;
+    if (i < ns && b < B) {
+      const int m = rows[i];
+      if (m >= 0 && m < M) {
+        const int W = blockDim.x >> 6;
+        float t = red[0][j];
+        for (int w = 1; w < W; ++w) t += red[w][j];
+        y[(size_t)m * B + b] += f16_bits_to_float(s[i]) * t;
+      }
     }
   }
 }
@@ -271,24 +312,26 @@ hipError_t launch_salient_mfma(const int32_t* rows, int ns, const int8_t* q, con
 
 hipError_t launch_salient_apply(const int32_t* rows, int ns, const int8_t* q, const uint16_t* s, int M, int N,
                                 const void* x, int xdt, int B, float* y, hipStream_t st) {
-  // Both batched kernels move about 13-14 bytes per clock into each compute
-  // unit, so the time follows the bytes of the busiest one: a workgroup per
-  // row reads x (32 N bytes per 16 batch columns) on each of up to 256
-  // compute units and twice that where a unit takes two rows; 16 rows per
-  // workgroup read x and 16 rows of q (48 N).  Measured at B = 16: 138 rows
-  // of 5120 take 8.0 us one per workgroup and 10.1 us on the matrix cores;
-  // 287 rows of 8192 take 16.7 and 14.6 us.
+  // Batches: more than 256 protected rows on the matrix cores (16 rows per
+  // workgroup, x read once per 16 rows); else four rows and four batch
+  // columns per workgroup; else one row and 16 columns with one load per
+  // value.  Measured (graph replay): 287 rows of 8192 at B = 16 take 15.8 us
+  // on the matrix cores and 16.8 us four by four; 138 rows of 5120 take
+  // 7.9 us four by four and 10.1 us on the matrix cores; at B = 4 four by
+  // four takes 7.3 us (138 x 5120), 10.0 us (287 x 8192) and 10.7 us
+  // (51 x 13824), against 12.5, 25.4 and 21.7 us one row at a time.
   if (ns > 256 && salient_mfma_ok(ns, N, q, x, xdt, B))
     return launch_salient_mfma(rows, ns, q, s, M, N, x, xdt, B, y, st);
-  if (B > 1) {  // a workgroup per protected row and 16 batch columns
-    const bool vec = xdt != BSG_F32 && B % 8 == 0 && aligned(x, 16);
+  if (B > 1 && B % 4 == 0 && xdt != BSG_F32 && aligned(x, 8)) {
+    const dim3 grid((ns + 3) / 4, B / 4);
+    const int threads = std::min(1024, std::max(64, (N / kSalCols + 63) / 64 * 64));  // about kSalCols columns each
+    hipLaunchKernelGGL(k_salient_rb<4>, grid, dim3(threads), 0, st, rows, q, s, ns, M, N, x, xdt, B, y);
+    return hipGetLastError();
+  }
+  if (B > 1) {
     const dim3 grid(ns, (B + 15) / 16);
-    // VEC: about kSalCols columns each, else about 4
-    const int threads = std::min(1024, std::max(64, (N / (vec ? kSalCols : 4) + 63) / 64 * 64));
-    if (vec)
-      hipLaunchKernelGGL(k_salient_bt<true>, grid, dim3(threads), 0, st, rows, q, s, ns, M, N, x, xdt, B, y);
-    else
-      hipLaunchKernelGGL(k_salient_bt<false>, grid, dim3(threads), 0, st, rows, q, s, ns, M, N, x, xdt, B, y);
+    const int threads = std::min(1024, std::max(64, (N / 4 + 63) / 64 * 64));  // about 4 columns each
+    hipLaunchKernelGGL(k_salient_bt, grid, dim3(threads), 0, st, rows, q, s, ns, M, N, x, xdt, B, y);
     return hipGetLastError();
   }
   const bool vec = xdt != BSG_F32 && N % 16 == 0 && aligned(q, 16) && aligned(x, 16);

@@ -15,8 +15,8 @@
 // own LDS tile for the B operand, as in the batched sign product.  The
 // partial tiles are summed through LDS in a fixed order (no atomics).
 // Rows past ns and columns past N load zero (buffer loads past the end).
-// Chosen for more than 256 protected rows, where a workgroup per row would
-// put two rows on some compute units.
+// Chosen for more than 256 protected rows (B % 8 == 0), where it measured
+// faster than four rows and four batch columns per workgroup.
 #include <algorithm>
 
 #include "bsg_prod_mfma.h"

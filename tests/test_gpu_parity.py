@@ -232,14 +232,16 @@ def test_binlr_apply_matches_oracle(case):
 # ------------------------------------------------------------------ protected rows
 # More than 256 protected rows, B % 8 == 0, N % 8 == 0 and 16-bit x: 16 protected rows per workgroup
 # on the matrix cores (ragged row tiles, half-empty and several batch tiles, partial and single
-# 128-column runs); otherwise one workgroup per row (hoisted loads when B % 8 == 0)
+# 128-column runs); otherwise B % 4 == 0 with 16-bit x: four rows and four batch columns per
+# workgroup (ragged row groups); otherwise one row per workgroup and one load per value
 SAL_CASES = [(256, 256, 3, 1, "bf16"), (13824, 5120, 138, 1, "bf16"), (100, 100, 5, 2, "bf16"),
              (5120, 13824, 51, 16, "bf16"), (64, 32, 64, 1, "bf16"), (64, 48, 3, 1, "bf16"),
              (300, 100, 7, 1, "bf16"), (5120, 13824, 51, 1, "bf16"), (13824, 5120, 138, 16, "bf16"),
              (13824, 5120, 138, 16, "f16"), (300, 200, 20, 8, "bf16"), (64, 40, 17, 24, "f16"),
              (100, 100, 5, 16, "bf16"), (200, 256, 9, 12, "f16"),
              (28672, 8192, 287, 16, "bf16"), (2000, 520, 300, 16, "f16"), (1000, 4104, 270, 32, "bf16"),
-             (600, 40, 260, 8, "bf16"), (700, 100, 280, 16, "bf16")]
+             (600, 40, 260, 8, "bf16"), (700, 100, 280, 16, "bf16"), (300, 96, 11, 3, "bf16"),
+             (2000, 1000, 30, 4, "f16"), (600, 200, 270, 12, "bf16")]
 
 
 @pytest.mark.parametrize("case", SAL_CASES, ids=lambda c: "M%d_N%d_ns%d_B%d_%s" % c)
