@@ -25,16 +25,21 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8, int gsw) 
   // (one per compute unit) -- except for very tall matrices (>= 256 row
   // blocks of 64), which run 2 lanes per row (measured fastest on
   // 28672 x 8192).
+  // The int8 product at one batch column builds its bit planes once per
+  // workgroup for all its rows, so it takes the fewest lanes that give 192
+  // workgroups (measured: 14336 x 4096 at 1 lane per row, 224 workgroups,
+  // 8.9 us against 11.6 us at 2 lanes; 4096 x 4096 best at 4 lanes).
   const int forceQ = env_int("BSG_Q", 0);
   const bool tall = M >= 64 * 256;
+  const int minwg = (i8 && B == 1) ? 192 : 256;
   if (forceQ == 1 || forceQ == 2 || forceQ == 4) {
     p.Q = forceQ;
-  } else if (tall) {
+  } else if (tall && !(i8 && B == 1)) {
     p.Q = 2;
   } else {
     p.Q = 4;
     for (int qq = 1; qq <= 4; qq *= 2) {
-      if ((M + 64 / qq - 1) / (64 / qq) >= 256) {
+      if ((M + 64 / qq - 1) / (64 / qq) >= minwg) {
         p.Q = qq;
         break;
       }

@@ -164,7 +164,7 @@ def test_bs_gemv_one_hot_reads_every_column():
 
 # ------------------------------------------------------------------ int8 mode
 I8_CASES = [(1, 256, 256, 1), (2, 300, 544, 1), (3, 70, 96, 2), (2, 4096, 4096, 1), (2, 333, 2080, 16),
-            (1, 5, 14336, 3), (2, 129, 1056, 20)]
+            (1, 5, 14336, 3), (2, 129, 1056, 20), (2, 14336, 4096, 1), (1, 20000, 512, 1)]
 
 
 @pytest.mark.parametrize("case", I8_CASES, ids=lambda c: "K%d_M%d_N%d_B%d" % c)
