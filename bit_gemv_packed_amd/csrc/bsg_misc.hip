@@ -125,19 +125,24 @@ __global__ void __launch_bounds__(1024) k_salient_bt(const int32_t* __restrict__
 }
 
 // Four protected rows and four batch columns per workgroup (16-bit x, B % 4
-// == 0, x 8-byte aligned): 16 sums per thread, one 8-byte x load and four
-// q bytes per column n.  A thread issues the loads of up to kSalCols
-// columns before any product, so a row of up to kSalCols * 1024 columns
-// costs one round of memory latency (a loop that waited for each column's
-// loads cost about 2 us per column on 1024 threads); columns past N re-read
-// column N - 1 and rows past ns re-read row ns - 1, with weight 0.
+// == 0, x 8-byte aligned): 16 sums per thread.  QW (B == 4, N % 4 == 0, q
+// 4-byte aligned): a thread takes groups of 4 consecutive columns, with one
+// 4-byte q load per row and one 8-byte x load per column (B = 4: 138 rows of
+// 5120 in 6.7 against 7.3 us, 287 of 8192 in 9.2 against 9.9 us); else
+// single columns with one q byte per row.  A thread issues the loads of up to kSalCols columns
+// before any product, so a row of up to kSalCols * 1024 columns costs one
+// round of memory latency (a loop that waited for each column's loads cost
+// about 2 us per column on 1024 threads); columns past N re-read column
+// N - 1 and rows past ns re-read row ns - 1, with weight 0.
 constexpr int kSalCols = 8;
-template <int R>
+template <int R, bool QW>
 __global__ void __launch_bounds__(1024) k_salient_rb(const int32_t* __restrict__ rows, const int8_t* __restrict__ q,
                                                    const uint16_t* __restrict__ s, int ns, int M, int N,
                                                    const void* __restrict__ x, int xdt, int B, float* __restrict__ y) {
   constexpr int BC = 16 / R;  // batch columns per workgroup (4: one 8-byte load)
   static_assert(BC == 4, "one 8-byte x load per column");
+  constexpr int CG = QW ? 4 : 1;     // columns per group
+  constexpr int NGR = kSalCols / CG;  // groups per thread and round
   __shared__ float red[16][16];
   const int i0 = blockIdx.x * R, b0 = blockIdx.y * BC;
   float acc[16];
@@ -146,31 +151,36 @@ __global__ void __launch_bounds__(1024) k_salient_rb(const int32_t* __restrict__
   const int8_t* qr[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) qr[r] = q + (size_t)min(i0 + r, ns - 1) * N;
-  for (int n0 = threadIdx.x; n0 < N; n0 += kSalCols * blockDim.x) {
-    uint2 xv[kSalCols];
-    int qv[kSalCols][R];
+  const int NG = (N + CG - 1) / CG;
+  for (int g0 = threadIdx.x; g0 < NG; g0 += NGR * blockDim.x) {
+    uint2 xv[NGR][CG];
+    uint32_t qv[NGR][R];
 #pragma unroll
-    for (int u = 0; u < kSalCols; ++u) {
-      const int nc = min(n0 + u * (int)blockDim.x, N - 1);
-      xv[u] = *(const uint2*)((const uint16_t*)x + (size_t)nc * B + b0);
+    for (int u = 0; u < NGR; ++u) {
+      const int n = min(g0 + u * (int)blockDim.x, NG - 1) * CG;
 #pragma unroll
-      for (int r = 0; r < R; ++r) qv[u][r] = qr[r][nc];
+      for (int c = 0; c < CG; ++c) xv[u][c] = *(const uint2*)((const uint16_t*)x + (size_t)min(n + c, N - 1) * B + b0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) qv[u][r] = QW ? *(const uint32_t*)(qr[r] + n) : (uint32_t)(uint8_t)qr[r][n];
     }
 #pragma unroll
-    for (int u = 0; u < kSalCols; ++u) {
-      const bool in = n0 + u * (int)blockDim.x < N;
-      const uint32_t w[2] = {xv[u].x, xv[u].y};
-      float xf[BC];
+    for (int u = 0; u < NGR; ++u) {
+      const bool in = g0 + u * (int)blockDim.x < NG;
 #pragma unroll
-      for (int c = 0; c < BC; ++c) {
-        const uint16_t h = (uint16_t)(w[c >> 1] >> (16 * (c & 1)));
-        xf[c] = xdt == BSG_BF16 ? bf16_bits_to_float(h) : f16_bits_to_float(h);
-      }
+      for (int c = 0; c < CG; ++c) {
+        const uint32_t w[2] = {xv[u][c].x, xv[u][c].y};
+        float xf[BC];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float qf = in && i0 + r < ns ? (float)qv[u][r] : 0.0f;
+        for (int b = 0; b < BC; ++b) {
+          const uint16_t h = (uint16_t)(w[b >> 1] >> (16 * (b & 1)));
+          xf[b] = xdt == BSG_BF16 ? bf16_bits_to_float(h) : f16_bits_to_float(h);
+        }
 #pragma unroll
-        for (int c = 0; c < BC; ++c) acc[r * BC + c] = __builtin_fmaf(qf, xf[c], acc[r * BC + c]);
+        for (int r = 0; r < R; ++r) {
+          const float qf = in && i0 + r < ns ? (float)(int8_t)(qv[u][r] >> (8 * c)) : 0.0f;
+#pragma unroll
+          for (int b = 0; b < BC; ++b) acc[r * BC + b] = __builtin_fmaf(qf, xf[b], acc[r * BC + b]);
+        }
       }
     }
   }
@@ -325,7 +335,13 @@ hipError_t launch_salient_apply(const int32_t* rows, int ns, const int8_t* q, co
   if (B > 1 && B % 4 == 0 && xdt != BSG_F32 && aligned(x, 8)) {
     const dim3 grid((ns + 3) / 4, B / 4);
     const int threads = std::min(1024, std::max(64, (N / kSalCols + 63) / 64 * 64));  // about kSalCols columns each
-    hipLaunchKernelGGL(k_salient_rb<4>, grid, dim3(threads), 0, st, rows, q, s, ns, M, N, x, xdt, B, y);
+    // 4-column groups only at B = 4: a lane's x rows then lie 32 bytes from
+    // its neighbour's (16 cache lines per load); at B = 16, 128 bytes apart,
+    // they measured slower (13.5 against 11.5 us at 51 rows of 13824)
+    if (B == 4 && N % 4 == 0 && aligned(q, 4))
+      hipLaunchKernelGGL((k_salient_rb<4, true>), grid, dim3(threads), 0, st, rows, q, s, ns, M, N, x, xdt, B, y);
+    else
+      hipLaunchKernelGGL((k_salient_rb<4, false>), grid, dim3(threads), 0, st, rows, q, s, ns, M, N, x, xdt, B, y);
     return hipGetLastError();
   }
   if (B > 1) {

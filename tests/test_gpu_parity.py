@@ -241,7 +241,8 @@ SAL_CASES = [(256, 256, 3, 1, "bf16"), (13824, 5120, 138, 1, "bf16"), (100, 100,
              (100, 100, 5, 16, "bf16"), (200, 256, 9, 12, "f16"),
              (28672, 8192, 287, 16, "bf16"), (2000, 520, 300, 16, "f16"), (1000, 4104, 270, 32, "bf16"),
              (600, 40, 260, 8, "bf16"), (700, 100, 280, 16, "bf16"), (300, 96, 11, 3, "bf16"),
-             (2000, 1000, 30, 4, "f16"), (600, 200, 270, 12, "bf16")]
+             (2000, 1000, 30, 4, "f16"), (600, 200, 270, 12, "bf16"), (300, 98, 9, 8, "bf16"),
+             (500, 98, 7, 4, "bf16")]
 
 
 @pytest.mark.parametrize("case", SAL_CASES, ids=lambda c: "M%d_N%d_ns%d_B%d_%s" % c)
