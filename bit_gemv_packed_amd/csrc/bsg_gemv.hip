@@ -44,6 +44,11 @@ ProdPlan plan_prod(int K, int M, int N, int B, bool colscale, bool i8, int gsw) 
         break;
       }
     }
+    // 4 lanes per row with more than 256 workgroups (4096 < M < 8192): 2
+    // lanes, one round of workgroups with 32 rows each, measured faster
+    // than 16 rows in more than one round (5120 x 13824: 10.5 against
+    // 11.6 us; 5120 x 5120, K = 3: 7.55 against 7.73 us)
+    if (p.Q == 4 && !i8 && (M + 15) / 16 > 256) p.Q = 2;
   }
   p.RW = 64 / p.Q;
   const int KX = (colscale && !i8) ? K : 1;
