@@ -84,8 +84,10 @@ bool mfma_cg_ok(int B, int xdt, const void* x, bool colscale, int gsw, int M) {
 
 // One launch per 16 batch columns and per group of up to 4 bases (2 with
 // 2-byte x loads; later groups accumulate).  Row tiles per workgroup: 2 when
-// that still gives at least 256 workgroups (x is then read once per 32
-// rows), else 1.  Wavefronts: up to mfma_max_waves, each taking whole
+// one would give more than 256 workgroups (x is then read once per 32
+// rows, in one round of workgroups where M < 8192: at B = 16, 5120 x 5120,
+// K = 3 takes 12.6 against 17.0 us, 6144 x 4096 9.3 against 12.2 us), else
+// 1 (4096 x 4096: 7.4 against 9.3 us).  Wavefronts: up to mfma_max_waves, each taking whole
 // 4-step layout tiles.  With a0.np > 1 every launch covers the row tiles of
 // all projections a0.proj[0 .. np) in turn (4- or 8-value x loads only).
 hipError_t launch_prod_mfma(const ProdArgs& a0, hipStream_t st) {
@@ -104,7 +106,7 @@ hipError_t launch_prod_mfma(const ProdArgs& a0, hipStream_t st) {
     mt = 0;
     for (int i = 0; i < a0.np; ++i) mt += a0.proj[i].M;
   }
-  const int RT = VW == 1 ? 1 : mf_env("BSG_MF_RT", (mt + 31) / 32 >= 256 ? 2 : 1) >= 2 ? 2 : 1;
+  const int RT = VW == 1 ? 1 : mf_env("BSG_MF_RT", (mt + 15) / 16 > 256 ? 2 : 1) >= 2 ? 2 : 1;
   const int KG = VW == 1 ? 2 : 4;      // bases per launch
   int nwg = (a0.M + 16 * RT - 1) / (16 * RT);
   if (multi) {
